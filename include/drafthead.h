@@ -1,0 +1,148 @@
+/*
+ * drafthead.h — C-ABI of the MI355X (gfx950) reduced-vocabulary NVFP4 draft
+ * head.
+ *
+ * The method (page 1, "q38_draft.py", module docstring and load_draft_model;
+ * page 4, "Qwen3.8-27B-NVFP4-DGX-SPARK", section on why native MTP plateaus):
+ * a speculative drafter scores only a kept subset of the vocabulary.  The kept
+ * rows of the BF16 target lm_head are gathered, re-quantized to NVFP4, and
+ * every draft step runs a W4A16 GEMV of the hidden state against them, takes
+ * the argmax over the kept rows and maps the winning row back to a target id.
+ *
+ * Conventions shared by every entry point below
+ * ---------------------------------------------
+ *  - Pointers marked [device] are device memory of the current HIP device;
+ *    [host] pointers are ordinary host memory.  The caller owns every buffer;
+ *    the library allocates nothing, keeps no per-call state and never
+ *    synchronizes.  All device work is enqueued on `stream` (a hipStream_t
+ *    passed as void*; NULL is the null stream) and is complete only when the
+ *    caller synchronizes that stream.
+ *  - Layouts are row-major.  An NVFP4 head of n_rows x hidden is
+ *      packed [n_rows][hidden/2]  uint8: element k of a row sits in byte k/2,
+ *                                 low nibble for even k, high nibble for odd k;
+ *                                 a nibble is sign (bit 3) + e2m1 magnitude
+ *                                 index (bits 0-2) into {0,.5,1,1.5,2,3,4,6};
+ *      scales [n_rows][hidden/16] uint8: OCP E4M3 (e4m3fn) scale of the
+ *                                 16-element block k/16;
+ *      global_scale               one float32; an element decodes to
+ *                                 e2m1 * e4m3 * global_scale.
+ *    BF16 tensors are raw 16-bit patterns.  Row indices are int32.
+ *  - The row index dh_idx has n_rows entries, n_rows a multiple of 64: the
+ *    n_kept kept target ids in ascending order, then copies of dh_idx[0]
+ *    (page 1, load_draft_model pads the index so the NVFP4 GEMM row count is
+ *    a multiple of 64).  draft_head_build_index produces it.
+ *  - Workspace: device memory of at least draft_head_workspace_bytes() bytes,
+ *    zero-filled once by the caller before its first use.  The kernels leave
+ *    it zeroed again when they finish.  Calls that may run concurrently need
+ *    distinct workspaces.
+ *  - Every function returns DH_OK (0) or a negative DH_E* code; no C++
+ *    exception crosses this interface.  Arguments are checked on the host
+ *    before any device work is enqueued.  Ids outside [0, vocab) and
+ *    non-finite inputs are outside the contract and are not checked on the
+ *    device.
+ */
+#ifndef DRAFTHEAD_H
+#define DRAFTHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DH_OK 0
+#define DH_EINVAL (-1)     /* null pointer, bad size or shape */
+#define DH_EWORKSPACE (-2) /* workspace pointer null or too small */
+#define DH_EHIP (-3)       /* a HIP runtime call or kernel launch failed */
+
+#define DRAFTHEAD_ABI_VERSION 1
+
+int drafthead_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* drafthead_error_string(int status);
+
+/*
+ * Row index from a keep mask (page 1, load_draft_model: the kept ids come
+ * from the mask's nonzero entries; with no mask every id is kept; the list is
+ * padded to a multiple of 64 with copies of its first id).
+ *   keep_mask [host]  vocab bytes, nonzero = kept
+ *   dh_idx    [host]  out: capacity int32 slots
+ *   n_kept    [host]  out: number of kept ids
+ * Returns n_rows (>= 64) or DH_EINVAL (null pointer, vocab < 1, empty mask,
+ * capacity < n_rows).  Host only; touches no device.
+ */
+int64_t draft_head_build_index(const uint8_t* keep_mask, int64_t vocab,
+                               int32_t* dh_idx, int64_t capacity,
+                               int64_t* n_kept);
+
+/* Workspace bytes the calls below need for a head of n_rows rows at this
+ * batch size.  Returns 0 for n_rows < 1 or batch < 1. */
+size_t draft_head_workspace_bytes(int64_t n_rows, int64_t batch);
+
+/*
+ * Gather + NVFP4 quantization of the kept rows (page 3, "...MTP-NVFP4-h98k",
+ * "How it was built": global scale amax/(6*448), E4M3 block scales per 16
+ * elements, e2m1 codes rounded to nearest-even; page 1: the quantizer is fed
+ * the gathered rows W[dh_idx]).
+ *   w_bf16       [device] vocab x hidden BF16 target head
+ *   row_ids      [device] n_rows int32 ids in [0, vocab) (dh_idx)
+ *   packed       [device] out: n_rows x hidden/2
+ *   scales       [device] out: n_rows x hidden/16
+ *   global_scale [device] out: one float32
+ * Arithmetic (float32, round-to-nearest-even): amax over the gathered rows;
+ * gs = max(amax, 1e-12) / 2688; per block s = bmax / (6*gs) rounded to E4M3
+ * (saturating at 448); element code = e2m1 of x / (e4m3(s)*gs), sign kept.
+ * Errors: DH_EINVAL for null pointers, hidden < 16 or hidden % 16 != 0,
+ * n_rows < 1, vocab < 1; DH_EWORKSPACE; DH_EHIP.
+ */
+int nvfp4_quantize_rows(const void* w_bf16, int64_t vocab, int64_t hidden,
+                        const int32_t* row_ids, int64_t n_rows,
+                        uint8_t* packed, uint8_t* scales, float* global_scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy draft tokens (page 1, get_top_tokens: the argmax over the kept rows
+ * of the draft head's output, mapped through dh_idx).
+ *   packed, scales, global_scale [device] the NVFP4 head (layout above)
+ *   dh_idx   [device] n_rows int32
+ *   h_bf16   [device] batch x hidden BF16 hidden states
+ *   out_ids  [device] out: batch int32 target ids
+ * For each batch row b: logit_j = sum_k e2m1*e4m3*h[b,k] accumulated in
+ * float32 (the positive global scale does not change the argmax and is not
+ * applied); row = lowest j with the largest logit; out_ids[b] = dh_idx[row].
+ * Errors: DH_EINVAL for null pointers, hidden % 16 != 0, hidden < 16,
+ * n_rows < 64 or n_rows % 64 != 0, batch < 1 or batch > 64;
+ * DH_EWORKSPACE; DH_EHIP.
+ */
+int draft_head_top_tokens(const uint8_t* packed, const uint8_t* scales,
+                          const float* global_scale, const int32_t* dh_idx,
+                          int64_t n_rows, int64_t hidden, const void* h_bf16,
+                          int64_t batch, int32_t* out_ids, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Draft logits over the full vocabulary (page 1, compute_logits: the draft
+ * head's output in float32, written into a batch x vocab tensor filled with
+ * -inf at the kept ids; page 2, compute_logits does the same scatter).
+ *   out_logits [device] out: batch x vocab float32
+ * out[b, v] = -inf for every v not among dh_idx[0:n_kept];
+ * out[b, dh_idx[j]] = global_scale * logit_j (float32) for j < n_kept (the
+ * pad rows are not written).  dh_idx[0:n_kept] must be strictly ascending,
+ * as draft_head_build_index makes it.
+ * Errors: as draft_head_top_tokens, plus DH_EINVAL for n_kept < 1,
+ * n_kept > n_rows, vocab < n_kept.
+ */
+int draft_head_logits(const uint8_t* packed, const uint8_t* scales,
+                      const float* global_scale, const int32_t* dh_idx,
+                      int64_t n_rows, int64_t n_kept, int64_t hidden,
+                      int64_t vocab, const void* h_bf16, int64_t batch,
+                      float* out_logits, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRAFTHEAD_H */

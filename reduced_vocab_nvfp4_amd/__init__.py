@@ -1,0 +1,215 @@
+"""Python binding of the MI355X reduced-vocabulary NVFP4 draft head.
+
+Argument marshalling only: every function here checks tensor dtypes and
+devices, allocates outputs with torch when the caller does not pass them,
+and calls the C-ABI of ``libdrafthead.so`` (declared in include/drafthead.h)
+on the current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If the library is not built, importing the
+functions works but the first call raises.
+
+Method: page 1 ("q38_draft.py", load_draft_model / get_top_tokens /
+compute_logits) and page 3 ("...MTP-NVFP4-h98k", "How it was built", the
+NVFP4 recipe).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdrafthead.so")
+
+DH_OK = 0
+DH_EINVAL = -1
+DH_EWORKSPACE = -2
+DH_EHIP = -3
+
+
+class DraftHeadError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {error_string(status)} (status {status})")
+
+
+_lib = None
+_c_i64 = ctypes.c_int64
+_c_ptr = ctypes.c_void_p
+_c_size = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python __graft_entry__.py` "
+                "or reduced_vocab_nvfp4_amd._build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.drafthead_abi_version.restype = ctypes.c_int
+        L.drafthead_error_string.restype = ctypes.c_char_p
+        L.drafthead_error_string.argtypes = [ctypes.c_int]
+        L.draft_head_build_index.restype = _c_i64
+        L.draft_head_build_index.argtypes = [_c_ptr, _c_i64, _c_ptr, _c_i64,
+                                             _c_ptr]
+        L.draft_head_workspace_bytes.restype = _c_size
+        L.draft_head_workspace_bytes.argtypes = [_c_i64, _c_i64]
+        L.nvfp4_quantize_rows.restype = ctypes.c_int
+        L.nvfp4_quantize_rows.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr,
+                                          _c_i64, _c_ptr, _c_ptr, _c_ptr,
+                                          _c_ptr, _c_size, _c_ptr]
+        L.draft_head_top_tokens.restype = ctypes.c_int
+        L.draft_head_top_tokens.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                            _c_i64, _c_i64, _c_ptr, _c_i64,
+                                            _c_ptr, _c_ptr, _c_size, _c_ptr]
+        L.draft_head_logits.restype = ctypes.c_int
+        L.draft_head_logits.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                        _c_i64, _c_i64, _c_i64, _c_i64,
+                                        _c_ptr, _c_i64, _c_ptr, _c_ptr,
+                                        _c_size, _c_ptr]
+        _lib = L
+    return _lib
+
+
+def error_string(status: int) -> str:
+    return lib().drafthead_error_string(int(status)).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != DH_OK:
+        raise DraftHeadError(fn, rc)
+
+
+def _dev(t: torch.Tensor, name: str, dtype) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+# --------------------------------------------------------------- A1 index
+
+def draft_head_build_index(keep_mask) -> tuple[torch.Tensor, int]:
+    """Row index from a bool keep mask (host): (dh_idx int32 CPU tensor of
+    n_rows entries, n_kept)."""
+    m = keep_mask.cpu().numpy() if isinstance(keep_mask, torch.Tensor) \
+        else np.asarray(keep_mask)
+    m = np.ascontiguousarray(m.astype(np.uint8))
+    V = m.shape[0]
+    cap = V + 64
+    out = np.empty(cap, dtype=np.int32)
+    n_kept = ctypes.c_int64(0)
+    n = lib().draft_head_build_index(m.ctypes.data, V, out.ctypes.data, cap,
+                                     ctypes.addressof(n_kept))
+    if n < 0:
+        raise DraftHeadError("draft_head_build_index", int(n))
+    return torch.from_numpy(out[:n].copy()), int(n_kept.value)
+
+
+def draft_head_workspace_bytes(n_rows: int, batch: int) -> int:
+    return int(lib().draft_head_workspace_bytes(int(n_rows), int(batch)))
+
+
+def new_workspace(n_rows: int, batch: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for heads of n_rows rows up to this batch."""
+    n = draft_head_workspace_bytes(n_rows, batch)
+    if n == 0:
+        raise ValueError("invalid n_rows/batch for a workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------ A2 quantize
+
+def nvfp4_quantize_rows(w: torch.Tensor, row_ids: torch.Tensor, *,
+                        packed=None, scales=None, global_scale=None,
+                        workspace=None, stream=None):
+    """Gather W[row_ids] and quantize to NVFP4 on the GPU.
+    Returns (packed u8 [n,H/2], scales u8 [n,H/16], global_scale f32 [1])."""
+    V, H = w.shape
+    n = row_ids.shape[0]
+    dev = w.device
+    if packed is None:
+        packed = torch.empty((n, H // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((n, H // 16), dtype=torch.uint8, device=dev)
+    if global_scale is None:
+        global_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(max(n, 1), 1, dev)
+    rc = lib().nvfp4_quantize_rows(
+        _dev(w, "w", torch.bfloat16), V, H,
+        _dev(row_ids, "row_ids", torch.int32), n,
+        _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
+        _dev(global_scale, "global_scale", torch.float32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("nvfp4_quantize_rows", rc)
+    return packed, scales, global_scale
+
+
+# ------------------------------------------------------- A3+A4 top tokens
+
+def draft_head_top_tokens(packed, scales, global_scale, dh_idx, h, *,
+                          out_ids=None, workspace=None, stream=None):
+    """Greedy draft tokens: int32 [B] target ids."""
+    n, H2 = packed.shape
+    B, H = h.shape
+    dev = h.device
+    if out_ids is None:
+        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(n, B, dev)
+    rc = lib().draft_head_top_tokens(
+        _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
+        _dev(global_scale, "global_scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, H,
+        _dev(h, "h", torch.bfloat16), B,
+        _dev(out_ids, "out_ids", torch.int32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_top_tokens", rc)
+    return out_ids
+
+
+# ------------------------------------------------------------- A5 logits
+
+def draft_head_logits(packed, scales, global_scale, dh_idx, n_kept: int,
+                      vocab: int, h, *, out=None, workspace=None, stream=None):
+    """float32 [B, vocab] logits, -inf at ids that were not kept."""
+    n, H2 = packed.shape
+    B, H = h.shape
+    dev = h.device
+    if out is None:
+        out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(n, B, dev)
+    rc = lib().draft_head_logits(
+        _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
+        _dev(global_scale, "global_scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, int(n_kept), H, int(vocab),
+        _dev(h, "h", torch.bfloat16), B, _dev(out, "out", torch.float32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_logits", rc)
+    return out
+
+
+__all__ = [
+    "DraftHeadError", "lib", "error_string", "draft_head_build_index",
+    "draft_head_workspace_bytes", "new_workspace", "nvfp4_quantize_rows",
+    "draft_head_top_tokens", "draft_head_logits",
+]

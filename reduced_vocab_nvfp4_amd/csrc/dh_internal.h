@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel
+// launchers.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dh {
+
+// Workspace layout (bytes).  The caller zero-fills it once; every kernel
+// that uses a slot returns it to zero before the call's work ends.
+constexpr size_t WS_COUNTER = 0;     // uint32 argmax arrival counter
+constexpr size_t WS_AMAX = 4;        // uint32 amax bits (quantizers)
+constexpr size_t WS_PARTIALS = 256;  // uint64 (value, row) per block per batch
+constexpr int MAX_GRID = 4096;       // upper bound of any argmax grid
+constexpr int MAX_BATCH = 64;
+
+size_t workspace_bytes(int64_t n_rows, int64_t batch);
+
+// Properties of the current device, queried once per device.
+struct DeviceInfo {
+  int cus;
+  int lds_per_block;
+};
+hipError_t device_info(DeviceInfo* out);
+
+struct QuantArgs {
+  const uint16_t* w;
+  int64_t vocab, hidden;
+  const int32_t* ids;
+  int64_t n_rows;
+  uint8_t* packed;
+  uint8_t* scales;
+  float* global_scale;
+  uint8_t* ws;
+};
+hipError_t launch_nvfp4_quantize(const QuantArgs& a, hipStream_t s);
+
+struct GemvArgs {
+  const uint8_t* packed;
+  const uint8_t* scales;
+  const float* global_scale;
+  const int32_t* dh_idx;
+  int64_t n_rows, hidden;
+  const uint16_t* h;
+  int64_t batch;
+  // top-token mode
+  int32_t* out_ids;
+  // logits mode (out_logits != nullptr)
+  float* out_logits;
+  int64_t n_kept, vocab;
+  uint8_t* ws;
+};
+hipError_t launch_nvfp4_top_tokens(const GemvArgs& a, hipStream_t s);
+hipError_t launch_nvfp4_logits(const GemvArgs& a, hipStream_t s);
+
+}  // namespace dh

@@ -1,0 +1,127 @@
+"""The C-ABI library without a GPU: it loads, exports what the header
+declares, builds the row index exactly like the oracle, and rejects bad
+arguments on the host before any device work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import reduced_vocab_nvfp4_amd as dh
+from reduced_vocab_nvfp4_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for hdr in os.listdir(os.path.join(ROOT, "include")):
+        if not hdr.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", hdr)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(",
+                            text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"nvfp4_quantize_rows", "draft_head_top_tokens",
+            "draft_head_logits"} <= set(names)
+    L = ctypes.CDLL(dh.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared but not exported"
+    assert dh.lib().drafthead_abi_version() == 1
+    assert dh.error_string(dh.DH_EINVAL).startswith("invalid")
+
+
+@pytest.mark.parametrize("name", ["tiny", "flash_next_64k", "h98k_b16"])
+def test_build_index_matches_oracle(name):
+    keep = wl.keep_mask(wl.WORKLOADS[name])
+    got, n_kept = dh.draft_head_build_index(keep)
+    want, want_kept = oracle.build_index(keep)
+    assert n_kept == want_kept
+    assert np.array_equal(got.numpy(), want)
+
+
+def test_build_index_edge_cases():
+    for keep in ([True] * 64, [True] * 65, [False] * 99 + [True], [True]):
+        got, n = dh.draft_head_build_index(np.array(keep))
+        want, wn = oracle.build_index(np.array(keep))
+        assert n == wn and np.array_equal(got.numpy(), want)
+    with pytest.raises(dh.DraftHeadError):
+        dh.draft_head_build_index(np.zeros(50, bool))
+
+
+def test_workspace_bytes():
+    assert dh.draft_head_workspace_bytes(64064, 1) >= 256 + 8 * 1024
+    assert dh.draft_head_workspace_bytes(0, 1) == 0
+    assert dh.draft_head_workspace_bytes(64, 0) == 0
+    assert dh.draft_head_workspace_bytes(64, 65) == 0
+
+
+FAKE = 1 << 20  # an aligned non-null address that is never dereferenced
+
+
+def test_quantize_rejects_bad_arguments_on_the_host():
+    L = dh.lib()
+    ws = dh.draft_head_workspace_bytes(64, 1)
+    args = dict(w=FAKE, V=1000, H=256, ids=FAKE, n=64, p=FAKE, s=FAKE, g=FAKE,
+                ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.nvfp4_quantize_rows(a["w"], a["V"], a["H"], a["ids"], a["n"],
+                                     a["p"], a["s"], a["g"], a["ws"], a["wsb"],
+                                     None)
+    assert call(w=None) == dh.DH_EINVAL
+    assert call(ids=None) == dh.DH_EINVAL
+    assert call(H=24) == dh.DH_EINVAL
+    assert call(H=0) == dh.DH_EINVAL
+    assert call(n=0) == dh.DH_EINVAL
+    assert call(V=0) == dh.DH_EINVAL
+    assert call(w=FAKE + 2) == dh.DH_EINVAL
+    assert call(ws=None) == dh.DH_EWORKSPACE
+    assert call(wsb=ws - 1) == dh.DH_EWORKSPACE
+
+
+def test_top_tokens_and_logits_reject_bad_arguments_on_the_host():
+    L = dh.lib()
+    ws = dh.draft_head_workspace_bytes(128, 8)
+    base = dict(p=FAKE, s=FAKE, g=FAKE, idx=FAKE, n=128, H=256, h=FAKE, B=1,
+                out=FAKE, ws=FAKE, wsb=ws)
+
+    def top(**kw):
+        a = {**base, **kw}
+        return L.draft_head_top_tokens(a["p"], a["s"], a["g"], a["idx"], a["n"],
+                                       a["H"], a["h"], a["B"], a["out"], a["ws"],
+                                       a["wsb"], None)
+
+    def logits(n_kept=100, vocab=1000, **kw):
+        a = {**base, **kw}
+        return L.draft_head_logits(a["p"], a["s"], a["g"], a["idx"], a["n"],
+                                   n_kept, a["H"], vocab, a["h"], a["B"],
+                                   a["out"], a["ws"], a["wsb"], None)
+    for f in (top, logits):
+        assert f(p=None) == dh.DH_EINVAL
+        assert f(s=None) == dh.DH_EINVAL
+        assert f(g=None) == dh.DH_EINVAL
+        assert f(idx=None) == dh.DH_EINVAL
+        assert f(h=None) == dh.DH_EINVAL
+        assert f(out=None) == dh.DH_EINVAL
+        assert f(n=100) == dh.DH_EINVAL       # not a multiple of 64
+        assert f(n=0) == dh.DH_EINVAL
+        assert f(H=40) == dh.DH_EINVAL        # not a multiple of 16
+        assert f(H=0) == dh.DH_EINVAL
+        assert f(B=0) == dh.DH_EINVAL
+        assert f(B=65) == dh.DH_EINVAL
+        assert f(p=FAKE + 8) == dh.DH_EINVAL  # packed must be 16-byte aligned
+        assert f(ws=None) == dh.DH_EWORKSPACE
+        assert f(wsb=16) == dh.DH_EWORKSPACE
+    assert logits(n_kept=0) == dh.DH_EINVAL
+    assert logits(n_kept=129) == dh.DH_EINVAL
+    assert logits(vocab=50) == dh.DH_EINVAL
+    assert logits(out=FAKE + 4) == dh.DH_EINVAL
