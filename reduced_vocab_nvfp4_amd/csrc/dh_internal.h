@@ -10,10 +10,19 @@ namespace dh {
 
 // Workspace layout (bytes).  The caller zero-fills it once; every kernel
 // that uses a slot returns it to zero before the call's work ends.
-constexpr size_t WS_COUNTER = 0;     // uint32 argmax arrival counter
-constexpr size_t WS_AMAX = 4;        // uint32 amax bits (quantizers)
-constexpr size_t WS_PARTIALS = 256;  // uint64 (value, row) per block per batch
-constexpr int MAX_GRID = 4096;       // upper bound of any argmax grid
+//   WS_TOP                top-level arrival counter of the argmax finish
+//   WS_AMAX               amax bits of the quantizers
+//   WS_GROUP + g*WS_GSTEP arrival counter of block group g (g < ARRIVAL_GROUPS);
+//                         4 KB apart so that each sits in its own memory
+//                         channel: same-address atomics serialize
+//   WS_PARTIALS           uint64 (value, row) per block per batch row
+constexpr size_t WS_TOP = 0;
+constexpr size_t WS_AMAX = 64;
+constexpr int ARRIVAL_GROUPS = 32;
+constexpr size_t WS_GSTEP = 4096;
+constexpr size_t WS_GROUP = WS_GSTEP;
+constexpr size_t WS_PARTIALS = WS_GROUP + ARRIVAL_GROUPS * WS_GSTEP;
+constexpr int MAX_GRID = 4096;  // upper bound of any argmax grid
 constexpr int MAX_BATCH = 64;
 
 size_t workspace_bytes(int64_t n_rows, int64_t batch);

@@ -15,28 +15,26 @@
 // even k), scales [n_rows][hidden/16] E4M3.  The kernel is a stream over
 // hidden/2 + hidden/16 bytes per row, so HBM bandwidth bounds it at batch 1.
 //
-// Work mapping (fast path, hidden = 32*G*C): a wave is 64/G groups of G
-// lanes, one head row per group per iteration.  A "chunk" is 16 packed
-// bytes (32 weights, two scale blocks); lane g of a group owns chunks
-// g, g+G, ..., g+(C-1)G of every row, so
+// Batch-1 kernel (hidden = 32*G*C): a wave is 64/G groups of G lanes, one
+// head row per group per iteration.  A "chunk" is 16 packed bytes (32
+// weights, two scale blocks); lane g of a group owns chunks g, g+G, ...,
+// g+(C-1)G of every row, so
 //   * each 128-bit load instruction reads G*16 contiguous bytes per row
 //     (256 B for G=16): fully coalesced;
-//   * the lane's slice of h is the same for every row and, at batch 1, stays
-//     in VGPRs (C*16 registers of BF16 pairs) for the whole kernel; at
-//     batch > 1 it is read from LDS.
-// Weights are dequantized in registers: v_cvt_scalef32_pk_bf16_fp4 turns
-// one byte (two e2m1 codes, low nibble first) into a BF16 pair with scale
-// 1.0 (exact), v_dot2_f32_bf16 accumulates the pair against h, each
-// 16-element block's partial is multiplied by its E4M3 scale
-// (v_cvt_f32_fp8, exact), and a DPP reduction over the G lanes finishes the
-// row.  Row groups are double-buffered so one group's loads are in flight
-// while the previous one is computed.
+//   * the lane's slice of h is the same for every row: it is staged once per
+//     wave through LDS and then held in C*16 VGPRs for the whole kernel.
+// Weights are dequantized in registers: v_cvt_scalef32_pk_bf16_fp4 turns one
+// byte (two e2m1 codes, low nibble first) into a BF16 pair with scale 1.0
+// (exact), v_dot2_f32_bf16 accumulates the pair against h, each 16-element
+// block's partial is multiplied by its E4M3 scale (v_cvt_f32_fp8, exact),
+// and a DPP reduction over the G lanes finishes the row.  A ring of NB
+// register buffers keeps NB-1 row groups in flight while one is reduced.
 //
 // Argmax: every lane keeps (best value, its row) over the rows it saw in
 // ascending order; the block reduces them (wave shuffles, then LDS) to one
-// (value, row) partial per batch row, written to the workspace; the last
-// block to arrive (agent-scope acq_rel counter) reduces all partials, ties
-// going to the lowest row, writes dh_idx[row] and resets the counter.
+// (value, row) partial per batch row; the last block to arrive reduces all
+// partials, ties going to the lowest row, writes dh_idx[row] and resets the
+// arrival counter (see argmax_finish for the cross-block protocol).
 #include <limits.h>
 
 #include "dh_device.h"
@@ -45,8 +43,7 @@
 namespace dh {
 namespace {
 
-constexpr int THREADS = 256;
-constexpr int WAVES = THREADS / 64;
+constexpr int THREADS = 256;  // block size of the generic and fill kernels
 constexpr int LDS_BUDGET = 64 * 1024;
 
 struct KArgs {
@@ -104,18 +101,33 @@ __device__ __forceinline__ uint64_t pack_partial(float v, int r) {
   return ((uint64_t)(uint32_t)r << 32) | (uint64_t)__float_as_uint(v);
 }
 
-// Block-level (value,row) reduction, partial write, and the last block's
+// Block-level (value,row) reduction, the partial write and the last block's
 // final pass.  best_v/best_r are this lane's per-batch candidates.
-template <int B>
+//
+// Cross-block protocol.  Each block publishes its partials with agent-scope
+// atomic stores (performed at the device-coherent level, past the per-XCD
+// L2) and waits for them to complete (s_waitcnt vmcnt(0)) before it counts
+// its arrival.  Arrivals are counted in two levels: block b adds to the
+// counter of group b % ARRIVAL_GROUPS (counters 4 KB apart, in different
+// memory channels: same-address atomics serialize at ~10 ns each, so one
+// counter for the whole grid costs microseconds), the last arriver of a
+// group adds to the top counter, and the block that completes the top count
+// has seen every other block arrive after its partials were complete; it
+// reads them with agent-scope atomic loads.  This is the release/acquire
+// pairing restricted to the only locations that cross blocks; a general
+// agent-scope release fence would also write back the whole L2 in every
+// block, which costs tens of microseconds over a grid.  Every counter is
+// returned to zero by the block that completes it.
+template <int B, int NT>
 __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
                                               int (&best_r)[B],
                                               const KArgs& a) {
-  __shared__ float sv[WAVES][B];
-  __shared__ int sr[WAVES][B];
+  constexpr int NW = NT / 64;
+  __shared__ float sv[NW][B];
+  __shared__ int sr[NW][B];
   __shared__ int is_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t* part = reinterpret_cast<uint64_t*>(a.ws + WS_PARTIALS);
-  uint32_t* counter = reinterpret_cast<uint32_t*>(a.ws + WS_COUNTER);
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     wave_argmax(best_v[b], best_r[b]);
@@ -129,7 +141,7 @@ __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
     for (int b = 0; b < B; ++b) {
       float v = sv[0][b];
       int r = sr[0][b];
-      for (int w = 1; w < WAVES; ++w)
+      for (int w = 1; w < NW; ++w)
         if (better(sv[w][b], sr[w][b], v, r)) {
           v = sv[w][b];
           r = sr[w][b];
@@ -138,18 +150,39 @@ __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
                          pack_partial(v, r), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
-    const uint32_t ticket = __hip_atomic_fetch_add(
-        counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (ticket == gridDim.x - 1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const uint32_t nb = gridDim.x;
+    const uint32_t ng = nb < ARRIVAL_GROUPS ? nb : ARRIVAL_GROUPS;
+    const uint32_t grp = blockIdx.x % ARRIVAL_GROUPS;
+    const uint32_t gsize = (nb - grp + ARRIVAL_GROUPS - 1) / ARRIVAL_GROUPS;
+    uint32_t* gcount =
+        reinterpret_cast<uint32_t*>(a.ws + WS_GROUP + grp * WS_GSTEP);
+    uint32_t* top = reinterpret_cast<uint32_t*>(a.ws + WS_TOP);
+    int last = 0;
+    const uint32_t t = __hip_atomic_fetch_add(gcount, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (t == gsize - 1) {
+      __hip_atomic_store(gcount, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t u = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      if (u == ng - 1) {
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        last = 1;
+      }
+    }
+    is_last = last;
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     float v = -INFINITY;
     int r = INT_MAX;
-    for (int i = threadIdx.x; i < (int)gridDim.x; i += THREADS) {
+    for (int i = threadIdx.x; i < (int)gridDim.x; i += NT) {
       const uint64_t p = __hip_atomic_load(&part[(int64_t)i * B + b],
                                            __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
@@ -171,7 +204,7 @@ __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
     const int b = threadIdx.x;
     float v = sv[0][b];
     int r = sr[0][b];
-    for (int w = 1; w < WAVES; ++w)
+    for (int w = 1; w < NW; ++w)
       if (better(sv[w][b], sr[w][b], v, r)) {
         v = sv[w][b];
         r = sr[w][b];
@@ -179,30 +212,27 @@ __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
     if (r < 0 || r >= a.n_rows) r = 0;  // only reachable with NaN inputs
     a.out_ids[b] = a.dh_idx[r];
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Copy h [B][hidden] into LDS as BF16 pairs.
-template <int B>
-__device__ __forceinline__ void stage_h(const uint16_t* h, int64_t hidden,
+template <int NT>
+__device__ __forceinline__ void stage_h(const uint16_t* h, int64_t count,
                                         uint32_t* hs) {
   const uint4* src = reinterpret_cast<const uint4*>(h);
   uint4* dst = reinterpret_cast<uint4*>(hs);
-  const int n = (int)(B * hidden / 8);
-  for (int t = threadIdx.x; t < n; t += THREADS) dst[t] = src[t];
+  const int n = (int)(count / 8);
+  for (int t = threadIdx.x; t < n; t += NT) dst[t] = src[t];
   __syncthreads();
 }
 
-template <int G, int C>
+template <int C>
 struct Rows {
   uint4 p[C];
   uint32_t s[C];
 };
 
 template <int G, int C>
-__device__ __forceinline__ void load_rows(Rows<G, C>& r, const KArgs& a,
+__device__ __forceinline__ void load_rows(Rows<C>& r, const KArgs& a,
                                           int64_t row, int g) {
   const uint4* prow =
       reinterpret_cast<const uint4*>(a.packed + row * (a.hidden / 2));
@@ -215,116 +245,143 @@ __device__ __forceinline__ void load_rows(Rows<G, C>& r, const KArgs& a,
   }
 }
 
-template <int G, int C, int B, bool LOGITS>
-__device__ __forceinline__ void compute_rows(
-    const Rows<G, C>& r, const KArgs& a, int64_t row, int g,
-    const uint32_t* hreg, const uint32_t* hs, float gs, float (&best_v)[B],
-    int (&best_r)[B]) {
-  float acc[B];
+template <int G, int C, bool LOGITS>
+__device__ __forceinline__ void compute_rows(const Rows<C>& r, const KArgs& a,
+                                             int64_t row, int g,
+                                             const uint32_t* hreg, float gs,
+                                             float& best_v, int& best_r) {
+  float acc = 0.0f;
 #pragma unroll
-  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < C; ++i) {
-    if constexpr (B == 1) {
-      acc[0] = chunk_dot(r.p[i], r.s[i], hreg + i * 16, acc[0]);
-    } else {
-      const int c = g + G * i;
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const uint4* hp4 =
-            reinterpret_cast<const uint4*>(hs + b * (a.hidden / 2) + c * 16);
-        uint32_t hp[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 v = hp4[q];
-          hp[4 * q + 0] = v.x;
-          hp[4 * q + 1] = v.y;
-          hp[4 * q + 2] = v.z;
-          hp[4 * q + 3] = v.w;
-        }
-        acc[b] = chunk_dot(r.p[i], r.s[i], hp, acc[b]);
-      }
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    const float v = group_sum<G>(acc[b]);
-    if constexpr (LOGITS) {
-      if (g == 0 && row < a.n_kept)
-        a.out_logits[b * a.vocab + a.dh_idx[row]] = v * gs;
-    } else {
-      // rows reach a lane in ascending order: strict > keeps the lowest
-      if (v > best_v[b]) {
-        best_v[b] = v;
-        best_r[b] = (int)row;
-      }
-    }
+  for (int i = 0; i < C; ++i) acc = chunk_dot(r.p[i], r.s[i], hreg + i * 16, acc);
+  const float v = group_sum<G>(acc);
+  if constexpr (LOGITS) {
+    if (g == 0 && row < a.n_kept) a.out_logits[a.dh_idx[row]] = v * gs;
+  } else if (v > best_v) {
+    // rows reach a lane in ascending order: strict > keeps the lowest
+    best_v = v;
+    best_r = (int)row;
   }
 }
 
-template <int G, int C, int B, bool LOGITS>
-__global__ __launch_bounds__(THREADS) void k_nvfp4_fast(const KArgs a) {
+// Batch-1 kernel: G lanes per row, C chunks per lane, NB register buffers,
+// NT threads per block.
+template <int G, int C, bool LOGITS, int NB, int NT>
+__global__ __launch_bounds__(NT) void k_nvfp4_b1(const KArgs a) {
   constexpr int R = 64 / G;  // rows per wave iteration
-  extern __shared__ uint32_t hs[];
+  constexpr int NW = NT / 64;
+  constexpr int HU4 = 4 * G * C;  // h as uint4 (hidden = 32*G*C BF16)
+  static_assert(HU4 % 64 == 0 || HU4 < 64, "h staging covers HU4 exactly");
+  __shared__ uint4 hl[NW][HU4 < 64 ? 64 : HU4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane / G, g = lane % G;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
-  uint32_t hreg[B == 1 ? C * 16 : 1];
-  if constexpr (B == 1) {
-    const uint4* h4 = reinterpret_cast<const uint4*>(a.h);
+  // Row groups are dealt to the grid's waves round-robin (grid stride):
+  // wave w of the grid takes groups w, w + TW, w + 2 TW, ...  The per-wave
+  // trip count is wave-uniform so loop control stays scalar.
+  const int64_t T = a.n_rows / R;
+  const int64_t TW = (int64_t)gridDim.x * NW;
+  const int64_t first = (int64_t)blockIdx.x * NW + wv;
+  const int n_it = first < T ? (int)((T - first + TW - 1) / TW) : 0;
+
+  // A ring of NB register buffers: the loads of group it+NB-1 are issued
+  // before group it is reduced, so NB-1 groups stay in flight.  The trip
+  // count is rounded up to a multiple of NB and row indices past the wave's
+  // last group are clamped to it: every load in the loop is unconditional
+  // (which keeps the compiler's wait counts exact), the surplus loads hit in
+  // L2, and reducing a duplicate of an already-seen row changes neither the
+  // argmax (same value, same row) nor the logits (same value, same slot).
+  // (A wave without row groups, possible only on tiny heads, reads group 0
+  // in its prologue and never reduces it.)
+  const int n_pad = (n_it + NB - 1) / NB * NB;
+  const int64_t base = n_it > 0 ? first : 0;
+  const int last = n_it > 0 ? n_it - 1 : 0;
+  auto row_of = [&](int it) {
+    const int c = it < last ? it : last;
+    return (base + (int64_t)c * TW) * R + grp;
+  };
+  // Prologue.  h is copied straight into this wave's LDS slice with
+  // global_load_lds_dwordx4 (lane i's 16 bytes land at slice + 16*i; no
+  // VGPRs, no block barrier), then the first weight row groups are issued,
+  // so only h has to arrive before the ring starts.  Every lane then keeps
+  // its C chunks of h in VGPRs.
+  constexpr int HJ = (HU4 + 63) / 64;  // h copies per lane
+  const uint4* h4 = reinterpret_cast<const uint4*>(a.h);
+  // lanes past the end of h (only when HU4 < 64) re-read its last uint4
+  const int hl0 = (HU4 % 64 == 0 || lane < HU4) ? lane : HU4 - 1;
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
+  for (int j = 0; j < HJ; ++j) {
+    // global_load_lds_dwordx4: M0 holds the wave's LDS destination.  It is
+    // issued as inline assembly so that the compiler's wait-count pass,
+    // which does not order LDS reads after these copies correctly, leaves
+    // them alone; the explicit wait below covers them.
+    const uint32_t lds_dst = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) void*)(&hl[wv][64 * j]));
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(h4 + hl0 + 64 * j), "s"(lds_dst)
+        : "memory", "m0");
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  Rows<C> buf[NB];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 v = h4[(g + G * i) * 4 + q];
-        hreg[i * 16 + 4 * q + 0] = v.x;
-        hreg[i * 16 + 4 * q + 1] = v.y;
-        hreg[i * 16 + 4 * q + 2] = v.z;
-        hreg[i * 16 + 4 * q + 3] = v.w;
-      }
+  for (int k = 0; k < NB - 1; ++k) load_rows<G, C>(buf[k], a, row_of(k), g);
+  // Memory loads retire in issue order, so once no more than the weight
+  // loads just issued are outstanding, the h copies have landed in LDS.
+  // (The wait is explicit: the compiler does not order LDS reads after
+  // global_load_lds on its own.)  The "memory" clobber keeps the LDS reads
+  // below it.
+  constexpr int WEIGHT_LOADS = (NB - 1) * 2 * C;
+  static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WEIGHT_LOADS) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t hreg[C * 16];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = hl[wave][(g + G * i) * 4 + q];
+      hreg[i * 16 + 4 * q + 0] = v.x;
+      hreg[i * 16 + 4 * q + 1] = v.y;
+      hreg[i * 16 + 4 * q + 2] = v.z;
+      hreg[i * 16 + 4 * q + 3] = v.w;
     }
-  } else {
-    stage_h<B>(a.h, a.hidden, hs);
   }
   const float gs = LOGITS ? *a.global_scale : 1.0f;
+  float best_v = -INFINITY;
+  int best_r = INT_MAX;
 
-  float best_v[B];
-  int best_r[B];
+  if (n_it > 0) {
+    for (int it = 0; it < n_pad; it += NB) {
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    best_v[b] = -INFINITY;
-    best_r[b] = INT_MAX;
+      for (int k = 0; k < NB; ++k) {
+        load_rows<G, C>(buf[(k + NB - 1) % NB], a, row_of(it + k + NB - 1), g);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_rows<G, C, LOGITS>(buf[k], a, row_of(it + k), g, hreg, gs,
+                                   best_v, best_r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
-
-  const int64_t T = a.n_rows / R;  // row groups
-  const int64_t rg0 = (int64_t)blockIdx.x * T / gridDim.x;
-  const int64_t rg1 = (int64_t)(blockIdx.x + 1) * T / gridDim.x;
-  Rows<G, C> ra, rb;
-  int64_t rg = rg0 + wave;
-  if (rg < rg1) load_rows<G, C>(ra, a, rg * R + grp, g);
-  while (rg < rg1) {
-    int64_t rn = rg + WAVES;
-    if (rn < rg1) load_rows<G, C>(rb, a, rn * R + grp, g);
-    compute_rows<G, C, B, LOGITS>(ra, a, rg * R + grp, g, hreg, hs, gs,
-                                  best_v, best_r);
-    rg = rn;
-    if (rg >= rg1) break;
-    rn = rg + WAVES;
-    if (rn < rg1) load_rows<G, C>(ra, a, rn * R + grp, g);
-    compute_rows<G, C, B, LOGITS>(rb, a, rg * R + grp, g, hreg, hs, gs,
-                                  best_v, best_r);
-    rg = rn;
+  if constexpr (!LOGITS) {
+    float bv[1] = {best_v};
+    int br[1] = {best_r};
+    argmax_finish<1, NT>(bv, br, a);
   }
-  if constexpr (!LOGITS) argmax_finish<B>(best_v, best_r, a);
 }
 
-// Any hidden % 16 == 0: one row per wave iteration, 8-byte (one block)
-// units strided over the 64 lanes, h for every batch row in LDS.
+// Any hidden % 16 == 0 and batch slices of 1-8 rows: one head row per wave
+// iteration, 8-byte (one block) units strided over the 64 lanes, h for
+// every batch row in LDS.
 template <int B, bool LOGITS>
 __global__ __launch_bounds__(THREADS) void k_nvfp4_generic(const KArgs a) {
+  constexpr int NW = THREADS / 64;
   extern __shared__ uint32_t hs[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  stage_h<B>(a.h, a.hidden, hs);
+  stage_h<THREADS>(a.h, B * a.hidden, hs);
   const float gs = LOGITS ? *a.global_scale : 1.0f;
   float best_v[B];
   int best_r[B];
@@ -336,7 +393,7 @@ __global__ __launch_bounds__(THREADS) void k_nvfp4_generic(const KArgs a) {
   const int64_t nblk = a.hidden / 16;
   const int64_t r0 = (int64_t)blockIdx.x * a.n_rows / gridDim.x;
   const int64_t r1 = (int64_t)(blockIdx.x + 1) * a.n_rows / gridDim.x;
-  for (int64_t row = r0 + wave; row < r1; row += WAVES) {
+  for (int64_t row = r0 + wave; row < r1; row += NW) {
     const uint2* prow =
         reinterpret_cast<const uint2*>(a.packed + row * (a.hidden / 2));
     const uint8_t* srow = a.scales + row * nblk;
@@ -364,7 +421,7 @@ __global__ __launch_bounds__(THREADS) void k_nvfp4_generic(const KArgs a) {
       }
     }
   }
-  if constexpr (!LOGITS) argmax_finish<B>(best_v, best_r, a);
+  if constexpr (!LOGITS) argmax_finish<B, THREADS>(best_v, best_r, a);
 }
 
 __global__ __launch_bounds__(THREADS) void k_fill_neg_inf(float* out,
@@ -387,34 +444,39 @@ typedef void (*KernelFn)(const KArgs);
 struct Variant {
   KernelFn fn;
   int rows_per_iter;  // rows a wave covers per iteration
+  int threads;
   bool fast;
 };
 
-template <int G, int C, int B, bool L>
-Variant fast_variant() {
-  return Variant{k_nvfp4_fast<G, C, B, L>, 64 / G, true};
+// Batch-1 kernel shape: two register buffers, 256-thread blocks (the
+// occupancy query then fits three blocks per CU at <= 168 VGPRs).
+constexpr int RING = 2;
+constexpr int B1_THREADS = 256;
+
+template <int G, int C, bool L>
+Variant b1_variant() {
+  return Variant{k_nvfp4_b1<G, C, L, RING, B1_THREADS>, 64 / G, B1_THREADS,
+                 true};
 }
 
 template <bool L>
 bool pick_variant(int64_t hidden, int bc, Variant* v) {
-  // The register-resident fast path serves batch 1 (the draft step); batch
-  // slices of 2-8 rows use the LDS-staged kernel.
   if (bc == 1 && hidden % 32 == 0) {
     switch (hidden / 32) {  // 16-byte chunks per row = G * C
-      case 8: *v = fast_variant<8, 1, 1, L>(); return true;
-      case 16: *v = fast_variant<16, 1, 1, L>(); return true;
-      case 32: *v = fast_variant<32, 1, 1, L>(); return true;
-      case 64: *v = fast_variant<64, 1, 1, L>(); return true;
-      case 80: *v = fast_variant<16, 5, 1, L>(); return true;
-      case 128: *v = fast_variant<32, 4, 1, L>(); return true;
-      case 160: *v = fast_variant<32, 5, 1, L>(); return true;
+      case 8: *v = b1_variant<8, 1, L>(); return true;
+      case 16: *v = b1_variant<16, 1, L>(); return true;
+      case 32: *v = b1_variant<32, 1, L>(); return true;
+      case 64: *v = b1_variant<64, 1, L>(); return true;
+      case 80: *v = b1_variant<16, 5, L>(); return true;
+      case 128: *v = b1_variant<32, 4, L>(); return true;
+      case 160: *v = b1_variant<32, 5, L>(); return true;
     }
   }
   switch (bc) {
-    case 1: *v = Variant{k_nvfp4_generic<1, L>, 1, false}; return true;
-    case 2: *v = Variant{k_nvfp4_generic<2, L>, 1, false}; return true;
-    case 4: *v = Variant{k_nvfp4_generic<4, L>, 1, false}; return true;
-    case 8: *v = Variant{k_nvfp4_generic<8, L>, 1, false}; return true;
+    case 1: *v = Variant{k_nvfp4_generic<1, L>, 1, THREADS, false}; return true;
+    case 2: *v = Variant{k_nvfp4_generic<2, L>, 1, THREADS, false}; return true;
+    case 4: *v = Variant{k_nvfp4_generic<4, L>, 1, THREADS, false}; return true;
+    case 8: *v = Variant{k_nvfp4_generic<8, L>, 1, THREADS, false}; return true;
   }
   return false;
 }
@@ -446,13 +508,14 @@ hipError_t launch_gemv(const GemvArgs& ga, bool logits, hipStream_t s) {
     const size_t lds = v.fast ? 0 : (size_t)bc * (size_t)ga.hidden * 2;
     int occ = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &occ, reinterpret_cast<const void*>(v.fn), THREADS, lds);
+        &occ, reinterpret_cast<const void*>(v.fn), v.threads, lds);
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
     // one resident wave of blocks, but at least one row group per wave
+    const int waves = v.threads / 64;
     const int64_t groups = ga.n_rows / v.rows_per_iter;
     int64_t grid = (int64_t)di.cus * occ;
-    const int64_t by_work = (groups + WAVES - 1) / WAVES;
+    const int64_t by_work = (groups + waves - 1) / waves;
     if (grid > by_work) grid = by_work;
     if (grid > MAX_GRID) grid = MAX_GRID;
     if (grid < 1) grid = 1;
@@ -471,7 +534,7 @@ hipError_t launch_gemv(const GemvArgs& ga, bool logits, hipStream_t s) {
     k.ws = ga.ws;
     void* kargs[] = {&k};
     e = hipLaunchKernel(reinterpret_cast<const void*>(v.fn),
-                        dim3((unsigned)grid), dim3(THREADS), kargs, lds, s);
+                        dim3((unsigned)grid), dim3(v.threads), kargs, lds, s);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
     b0 += bc;
