@@ -16,6 +16,9 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # quantizer bit-exactness: every float op rounds on its own
     "-ffp-contract=off",
+    # keep single-lane ticket fetches as issued: the atomic optimizer would
+    # rewrite them and read their result right away
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -62,6 +62,8 @@ enum : int {
   DPP_QUAD_2301 = 0x4E,      // quad_perm [2,3,0,1]
   DPP_ROW_HALF_MIRROR = 0x141,
   DPP_ROW_MIRROR = 0x140,
+  DPP_ROW_BCAST15 = 0x142,   // lane 15 of each row to the next row
+  DPP_ROW_BCAST31 = 0x143,   // lane 31 to rows 2 and 3
 };
 
 template <int CTRL>
@@ -89,17 +91,32 @@ __device__ __forceinline__ bool better(float v, int r, float bv, int br) {
   return v > bv || (v == bv && r < br);
 }
 
-// (value, row) argmax over the whole wave; every lane ends with the result.
-__device__ __forceinline__ void wave_argmax(float& v, int& r) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float ov = __shfl_xor(v, off, 64);
-    int orow = __shfl_xor(r, off, 64);
-    if (better(ov, orow, v, r)) {
-      v = ov;
-      r = orow;
-    }
+// (value, row) argmax over the whole wave with DPP moves (no LDS round
+// trips): quad swaps and row mirrors give every lane its 16-lane row's best,
+// row_bcast15 / row_bcast31 fold rows 0..3 into row 3, and lane 63's result
+// is broadcast.  The order "larger value, then lower row" is a total order,
+// so the combination order does not matter.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(float& v, int& r) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+  const int orow =
+      __builtin_amdgcn_update_dpp(r, r, CTRL, ROW_MASK, 0xF, false);
+  if (better(ov, orow, v, r)) {
+    v = ov;
+    r = orow;
   }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& r) {
+  argmax_step<DPP_QUAD_1032, 0xF>(v, r);
+  argmax_step<DPP_QUAD_2301, 0xF>(v, r);
+  argmax_step<DPP_ROW_HALF_MIRROR, 0xF>(v, r);
+  argmax_step<DPP_ROW_MIRROR, 0xF>(v, r);
+  argmax_step<DPP_ROW_BCAST15, 0xA>(v, r);
+  argmax_step<DPP_ROW_BCAST31, 0xC>(v, r);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  r = __builtin_amdgcn_readlane(r, 63);
 }
 
 }  // namespace dh

@@ -288,9 +288,8 @@ __global__ __launch_bounds__(NT) void k_nvfp4_b1(const KArgs a) {
   // before group it is reduced, so NB-1 groups stay in flight.  The trip
   // count is rounded up to a multiple of NB and row indices past the wave's
   // last group are clamped to it: every load in the loop is unconditional
-  // (which keeps the compiler's wait counts exact), the surplus loads hit in
-  // L2, and reducing a duplicate of an already-seen row changes neither the
-  // argmax (same value, same row) nor the logits (same value, same slot).
+  // (which keeps the compiler's wait counts exact) and the surplus loads hit
+  // in L2; the reduction of those padded iterations is skipped.
   // (A wave without row groups, possible only on tiny heads, reads group 0
   // in its prologue and never reduces it.)
   const int n_pad = (n_it + NB - 1) / NB * NB;
@@ -360,8 +359,9 @@ __global__ __launch_bounds__(NT) void k_nvfp4_b1(const KArgs a) {
       for (int k = 0; k < NB; ++k) {
         load_rows<G, C>(buf[(k + NB - 1) % NB], a, row_of(it + k + NB - 1), g);
         __builtin_amdgcn_sched_barrier(0);
-        compute_rows<G, C, LOGITS>(buf[k], a, row_of(it + k), g, hreg, gs,
-                                   best_v, best_r);
+        if (it + k < n_it)  // wave-uniform: padded iterations only load
+          compute_rows<G, C, LOGITS>(buf[k], a, row_of(it + k), g, hreg, gs,
+                                     best_v, best_r);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
