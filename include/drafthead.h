@@ -17,7 +17,10 @@
  *    synchronizes.  All device work is enqueued on `stream` (a hipStream_t
  *    passed as void*; NULL is the null stream) and is complete only when the
  *    caller synchronizes that stream.
- *  - Layouts are row-major.  An NVFP4 head of n_rows x hidden is
+ *  - Layouts are row-major.  Device pointers to weights, scales and hidden
+ *    states, and the logits output, must be 16-byte aligned (every torch
+ *    allocation is); ids, scalars and the workspace need 4 / 4 / 16 bytes.
+ *    An NVFP4 head of n_rows x hidden is
  *      packed [n_rows][hidden/2]  uint8: element k of a row sits in byte k/2,
  *                                 low nibble for even k, high nibble for odd k;
  *                                 a nibble is sign (bit 3) + e2m1 magnitude
@@ -26,7 +29,10 @@
  *                                 16-element block k/16;
  *      global_scale               one float32; an element decodes to
  *                                 e2m1 * e4m3 * global_scale.
- *    BF16 tensors are raw 16-bit patterns.  Row indices are int32.
+ *    A per-tensor E4M3 head is q [n_rows][hidden] OCP e4m3fn bytes and one
+ *    float32 scale; an element decodes to e4m3 * scale.  A BF16 head is
+ *    [n_rows][hidden] BF16.  BF16 tensors are raw 16-bit patterns.  Row
+ *    indices are int32.
  *  - The row index dh_idx has n_rows entries, n_rows a multiple of 64: the
  *    n_kept kept target ids in ascending order, then copies of dh_idx[0]
  *    (page 1, load_draft_model pads the index so the NVFP4 GEMM row count is
@@ -78,7 +84,7 @@ int64_t draft_head_build_index(const uint8_t* keep_mask, int64_t vocab,
                                int64_t* n_kept);
 
 /* Workspace bytes the calls below need for a head of n_rows rows at this
- * batch size.  Returns 0 for n_rows < 1 or batch < 1. */
+ * batch size.  Returns 0 for n_rows < 1, batch < 1 or batch > 64. */
 size_t draft_head_workspace_bytes(int64_t n_rows, int64_t batch);
 
 /*
@@ -94,8 +100,9 @@ size_t draft_head_workspace_bytes(int64_t n_rows, int64_t batch);
  * Arithmetic (float32, round-to-nearest-even): amax over the gathered rows;
  * gs = max(amax, 1e-12) / 2688; per block s = bmax / (6*gs) rounded to E4M3
  * (saturating at 448); element code = e2m1 of x / (e4m3(s)*gs), sign kept.
- * Errors: DH_EINVAL for null pointers, hidden < 16 or hidden % 16 != 0,
- * n_rows < 1, vocab < 1; DH_EWORKSPACE; DH_EHIP.
+ * Errors: DH_EINVAL for null pointers, hidden < 16, hidden > 16384 or
+ * hidden % 16 != 0, n_rows < 1, vocab < 1, packed not 8-byte aligned;
+ * DH_EWORKSPACE; DH_EHIP.
  */
 int nvfp4_quantize_rows(const void* w_bf16, int64_t vocab, int64_t hidden,
                         const int32_t* row_ids, int64_t n_rows,
@@ -113,8 +120,8 @@ int nvfp4_quantize_rows(const void* w_bf16, int64_t vocab, int64_t hidden,
  * float32 (the positive global scale does not change the argmax and is not
  * applied); row = lowest j with the largest logit; out_ids[b] = dh_idx[row].
  * Errors: DH_EINVAL for null pointers, hidden % 16 != 0, hidden < 16,
- * n_rows < 64 or n_rows % 64 != 0, batch < 1 or batch > 64;
- * DH_EWORKSPACE; DH_EHIP.
+ * hidden > 16384, n_rows < 64 or n_rows % 64 != 0, batch < 1 or batch > 64,
+ * misaligned pointers; DH_EWORKSPACE; DH_EHIP.
  */
 int draft_head_top_tokens(const uint8_t* packed, const uint8_t* scales,
                           const float* global_scale, const int32_t* dh_idx,
@@ -140,6 +147,77 @@ int draft_head_logits(const uint8_t* packed, const uint8_t* scales,
                       int64_t vocab, const void* h_bf16, int64_t batch,
                       float* out_logits, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Per-tensor E4M3 head from the same gathered rows (page 2, "FP8 MTP draft
+ * stack for vLLM", _fp8_convert_draft_head: the FP8 head it ships scales the whole head by amax/448, divides, clamps to
+ * +-448 and casts to e4m3fn; page 3 lists the FP8 head next to the NVFP4 one).
+ *   w_bf16  [device] vocab x hidden BF16 target head
+ *   row_ids [device] n_rows int32 ids in [0, vocab)
+ *   q       [device] out: n_rows x hidden e4m3fn bytes
+ *   scale   [device] out: one float32
+ * Arithmetic (float32, round-to-nearest-even): amax over the gathered rows;
+ * scale = max(amax, 1e-12) / 448; q = e4m3(clamp(x / scale, -448, 448)),
+ * sign kept (0x80 for a negative zero quotient).
+ * Errors: as nvfp4_quantize_rows (q must be 8-byte aligned).
+ */
+int e4m3_quantize_rows_per_tensor(const void* w_bf16, int64_t vocab,
+                                  int64_t hidden, const int32_t* row_ids,
+                                  int64_t n_rows, uint8_t* q, float* scale,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * Greedy draft tokens of a per-tensor E4M3 head (page 1, get_top_tokens, as
+ * for the NVFP4 head; page 2's FP8 head).  Activations stay BF16 (W8A16):
+ * logit_j = sum_k e4m3(q[j,k]) * h[b,k] in float32, the scale (positive) is
+ * not applied; out_ids[b] = dh_idx[lowest j with the largest logit].
+ * Errors: as draft_head_top_tokens.
+ */
+int draft_head_top_tokens_e4m3(const uint8_t* q, const float* scale,
+                               const int32_t* dh_idx, int64_t n_rows,
+                               int64_t hidden, const void* h_bf16,
+                               int64_t batch, int32_t* out_ids,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Logits of a per-tensor E4M3 head (page 2, compute_logits): as
+ * draft_head_logits with out[b, dh_idx[j]] = scale * logit_j.
+ * Errors: as draft_head_logits.
+ */
+int draft_head_logits_e4m3(const uint8_t* q, const float* scale,
+                           const int32_t* dh_idx, int64_t n_rows,
+                           int64_t n_kept, int64_t hidden, int64_t vocab,
+                           const void* h_bf16, int64_t batch,
+                           float* out_logits, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy tokens of an unquantized BF16 head (page 4: the stock drafter reads
+ * the full BF16 lm_head every draft step; page 1, get_top_tokens).  For the
+ * stock head pass all vocab rows and the identity index.
+ *   w_bf16 [device] n_rows x hidden BF16 rows (row j scores id dh_idx[j])
+ * logit_j = sum_k w[j,k] * h[b,k] in float32; out_ids[b] = dh_idx[lowest j
+ * with the largest logit].
+ * Errors: as draft_head_top_tokens.
+ */
+int draft_head_top_tokens_bf16(const void* w_bf16, const int32_t* dh_idx,
+                               int64_t n_rows, int64_t hidden,
+                               const void* h_bf16, int64_t batch,
+                               int32_t* out_ids, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Logits of a BF16 head (page 1 and page 2, compute_logits): as
+ * draft_head_logits with out[b, dh_idx[j]] = logit_j.
+ * Errors: as draft_head_logits.
+ */
+int draft_head_logits_bf16(const void* w_bf16, const int32_t* dh_idx,
+                           int64_t n_rows, int64_t n_kept, int64_t hidden,
+                           int64_t vocab, const void* h_bf16, int64_t batch,
+                           float* out_logits, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

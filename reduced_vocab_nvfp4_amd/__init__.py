@@ -70,6 +70,26 @@ def lib() -> ctypes.CDLL:
                                         _c_i64, _c_i64, _c_i64, _c_i64,
                                         _c_ptr, _c_i64, _c_ptr, _c_ptr,
                                         _c_size, _c_ptr]
+        L.e4m3_quantize_rows_per_tensor.restype = ctypes.c_int
+        L.e4m3_quantize_rows_per_tensor.argtypes = [
+            _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr,
+            _c_size, _c_ptr]
+        L.draft_head_top_tokens_e4m3.restype = ctypes.c_int
+        L.draft_head_top_tokens_e4m3.argtypes = [
+            _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
+            _c_ptr, _c_size, _c_ptr]
+        L.draft_head_logits_e4m3.restype = ctypes.c_int
+        L.draft_head_logits_e4m3.argtypes = [
+            _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64, _c_ptr,
+            _c_i64, _c_ptr, _c_ptr, _c_size, _c_ptr]
+        L.draft_head_top_tokens_bf16.restype = ctypes.c_int
+        L.draft_head_top_tokens_bf16.argtypes = [
+            _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr,
+            _c_size, _c_ptr]
+        L.draft_head_logits_bf16.restype = ctypes.c_int
+        L.draft_head_logits_bf16.argtypes = [
+            _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64, _c_ptr, _c_i64,
+            _c_ptr, _c_ptr, _c_size, _c_ptr]
         _lib = L
     return _lib
 
@@ -208,8 +228,119 @@ def draft_head_logits(packed, scales, global_scale, dh_idx, n_kept: int,
     return out
 
 
+# ------------------------------------------- per-tensor E4M3 head (FP8)
+
+def e4m3_quantize_rows_per_tensor(w: torch.Tensor, row_ids: torch.Tensor, *,
+                                  q=None, scale=None, workspace=None,
+                                  stream=None):
+    """Gather W[row_ids] and quantize to E4M3 with one tensor scale.
+    Returns (q u8 [n,H], scale f32 [1])."""
+    V, H = w.shape
+    n = row_ids.shape[0]
+    dev = w.device
+    if q is None:
+        q = torch.empty((n, H), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(max(n, 1), 1, dev)
+    rc = lib().e4m3_quantize_rows_per_tensor(
+        _dev(w, "w", torch.bfloat16), V, H,
+        _dev(row_ids, "row_ids", torch.int32), n, _dev(q, "q", torch.uint8),
+        _dev(scale, "scale", torch.float32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("e4m3_quantize_rows_per_tensor", rc)
+    return q, scale
+
+
+def draft_head_top_tokens_e4m3(q, scale, dh_idx, h, *, out_ids=None,
+                               workspace=None, stream=None):
+    """Greedy draft tokens of an E4M3 head: int32 [B] target ids."""
+    n, H = q.shape
+    B = h.shape[0]
+    dev = h.device
+    if out_ids is None:
+        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(n, B, dev)
+    rc = lib().draft_head_top_tokens_e4m3(
+        _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, H,
+        _dev(h, "h", torch.bfloat16), B, _dev(out_ids, "out_ids", torch.int32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_top_tokens_e4m3", rc)
+    return out_ids
+
+
+def draft_head_logits_e4m3(q, scale, dh_idx, n_kept: int, vocab: int, h, *,
+                           out=None, workspace=None, stream=None):
+    """float32 [B, vocab] logits of an E4M3 head, -inf at ids not kept."""
+    n, H = q.shape
+    B = h.shape[0]
+    dev = h.device
+    if out is None:
+        out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(n, B, dev)
+    rc = lib().draft_head_logits_e4m3(
+        _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, int(n_kept), H, int(vocab),
+        _dev(h, "h", torch.bfloat16), B, _dev(out, "out", torch.float32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_logits_e4m3", rc)
+    return out
+
+
+# ------------------------------------------------------- BF16 (stock) head
+
+def draft_head_top_tokens_bf16(w, dh_idx, h, *, out_ids=None, workspace=None,
+                               stream=None):
+    """Greedy tokens of a BF16 head [n_rows, H] (row j scores dh_idx[j])."""
+    n, H = w.shape
+    B = h.shape[0]
+    dev = h.device
+    if out_ids is None:
+        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(n, B, dev)
+    rc = lib().draft_head_top_tokens_bf16(
+        _dev(w, "w", torch.bfloat16), _dev(dh_idx, "dh_idx", torch.int32), n,
+        H, _dev(h, "h", torch.bfloat16), B,
+        _dev(out_ids, "out_ids", torch.int32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_top_tokens_bf16", rc)
+    return out_ids
+
+
+def draft_head_logits_bf16(w, dh_idx, n_kept: int, vocab: int, h, *,
+                           out=None, workspace=None, stream=None):
+    """float32 [B, vocab] logits of a BF16 head, -inf at ids not kept."""
+    n, H = w.shape
+    B = h.shape[0]
+    dev = h.device
+    if out is None:
+        out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(n, B, dev)
+    rc = lib().draft_head_logits_bf16(
+        _dev(w, "w", torch.bfloat16), _dev(dh_idx, "dh_idx", torch.int32), n,
+        int(n_kept), H, int(vocab), _dev(h, "h", torch.bfloat16), B,
+        _dev(out, "out", torch.float32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_logits_bf16", rc)
+    return out
+
+
 __all__ = [
     "DraftHeadError", "lib", "error_string", "draft_head_build_index",
     "draft_head_workspace_bytes", "new_workspace", "nvfp4_quantize_rows",
     "draft_head_top_tokens", "draft_head_logits",
+    "e4m3_quantize_rows_per_tensor", "draft_head_top_tokens_e4m3",
+    "draft_head_logits_e4m3", "draft_head_top_tokens_bf16",
+    "draft_head_logits_bf16",
 ]

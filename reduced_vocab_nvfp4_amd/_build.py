@@ -1,6 +1,7 @@
 """Builds libdrafthead.so from csrc/*.hip with hipcc for gfx950."""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -27,19 +28,34 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(PKG, "csrc"), *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd: list[str]) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines()
                     if "not a recognized feature" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object in parallel, then links."""
+    obj_dir = os.path.join(ROOT, "_build", "drafthead")
+    os.makedirs(obj_dir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    jobs = []
+    for src in sources():
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        jobs.append((obj, [HIPCC, *compile_flags, *inc, "-c", src, "-o", obj]))
+    workers = min(len(jobs), os.cpu_count() or 1, 8)
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        errs = list(ex.map(lambda j: _run(j[1]), jobs))
+    tmp = LIB + ".tmp"
+    errs.append(_run([HIPCC, *HIP_FLAGS, *[o for o, _ in jobs], "-o", tmp]))
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e)
     os.replace(tmp, LIB)
     return LIB
 

@@ -5,6 +5,7 @@
 #include "drafthead.h"
 
 #include "dh_internal.h"
+#include "formats.h"
 
 namespace dh {
 
@@ -14,8 +15,10 @@ static bool aligned(const void* p, uintptr_t n) {
 
 size_t workspace_bytes(int64_t n_rows, int64_t batch) {
   if (n_rows < 1 || batch < 1 || batch > MAX_BATCH) return 0;
-  const int64_t slice = batch < 8 ? batch : 8;
-  return WS_PARTIALS + (size_t)MAX_GRID * (size_t)slice * sizeof(uint64_t);
+  // A batch of one runs the one-row kernels; any larger batch may run a
+  // kernel that keeps MAX_SLICE partials per block.
+  const int64_t slots = batch == 1 ? 1 : MAX_SLICE;
+  return WS_PARTIALS + (size_t)MAX_GRID * (size_t)slots * sizeof(uint64_t);
 }
 
 hipError_t device_info(DeviceInfo* out) {
@@ -45,19 +48,90 @@ hipError_t device_info(DeviceInfo* out) {
 
 static int status(hipError_t e) { return e == hipSuccess ? DH_OK : DH_EHIP; }
 
-// Shape and pointer checks shared by the GEMV entry points.
-static int check_head(const uint8_t* packed, const uint8_t* scales,
-                      const float* gs, const int32_t* dh_idx, int64_t n_rows,
-                      int64_t hidden, const void* h, int64_t batch,
-                      const void* ws, size_t ws_bytes) {
-  if (!packed || !scales || !gs || !dh_idx || !h) return DH_EINVAL;
+// Shape and pointer checks shared by the GEMV entry points.  `scales` is
+// checked only for NVFP4 and `scale` only for the scaled formats.
+static int check_head(int fmt, const void* w, const uint8_t* scales,
+                      const float* scale, const int32_t* dh_idx,
+                      int64_t n_rows, int64_t hidden, const void* h,
+                      int64_t batch, const void* ws, size_t ws_bytes) {
+  if (!w || !dh_idx || !h) return DH_EINVAL;
+  if (fmt == FMT_NVFP4 && (!scales || !aligned(scales, 16))) return DH_EINVAL;
+  if (fmt != FMT_BF16 && (!scale || !aligned(scale, 4))) return DH_EINVAL;
   if (hidden < 16 || hidden > 16384 || hidden % 16 != 0) return DH_EINVAL;
   if (n_rows < 64 || n_rows % 64 != 0 || n_rows > INT32_MAX) return DH_EINVAL;
   if (batch < 1 || batch > MAX_BATCH) return DH_EINVAL;
-  if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(h, 16) ||
-      !aligned(gs, 4) || !aligned(dh_idx, 4))
+  if (!aligned(w, 16) || !aligned(h, 16) || !aligned(dh_idx, 4))
     return DH_EINVAL;
   if (!ws || !aligned(ws, 16) || ws_bytes < workspace_bytes(n_rows, batch))
+    return DH_EWORKSPACE;
+  return DH_OK;
+}
+
+static int top_tokens(int fmt, const void* w, const uint8_t* scales,
+                      const float* scale, const int32_t* dh_idx,
+                      int64_t n_rows, int64_t hidden, const void* h,
+                      int64_t batch, int32_t* out_ids, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!out_ids || !aligned(out_ids, 4)) return DH_EINVAL;
+  const int rc = check_head(fmt, w, scales, scale, dh_idx, n_rows, hidden, h,
+                            batch, ws, ws_bytes);
+  if (rc != DH_OK) return rc;
+  GemvArgs a{};
+  a.fmt = fmt;
+  a.w = static_cast<const uint8_t*>(w);
+  a.scales = scales;
+  a.scale = scale;
+  a.dh_idx = dh_idx;
+  a.n_rows = n_rows;
+  a.hidden = hidden;
+  a.h = static_cast<const uint16_t*>(h);
+  a.batch = batch;
+  a.out_ids = out_ids;
+  a.ws = static_cast<uint8_t*>(ws);
+  return status(launch_gemv(a, static_cast<hipStream_t>(stream)));
+}
+
+static int logits(int fmt, const void* w, const uint8_t* scales,
+                  const float* scale, const int32_t* dh_idx, int64_t n_rows,
+                  int64_t n_kept, int64_t hidden, int64_t vocab, const void* h,
+                  int64_t batch, float* out, void* ws, size_t ws_bytes,
+                  void* stream) {
+  if (!out || !aligned(out, 16)) return DH_EINVAL;
+  if (n_kept < 1 || n_kept > n_rows || vocab < n_kept || vocab > INT32_MAX)
+    return DH_EINVAL;
+  const int rc = check_head(fmt, w, scales, scale, dh_idx, n_rows, hidden, h,
+                            batch, ws, ws_bytes);
+  if (rc != DH_OK) return rc;
+  GemvArgs a{};
+  a.fmt = fmt;
+  a.w = static_cast<const uint8_t*>(w);
+  a.scales = scales;
+  a.scale = scale;
+  a.dh_idx = dh_idx;
+  a.n_rows = n_rows;
+  a.hidden = hidden;
+  a.h = static_cast<const uint16_t*>(h);
+  a.batch = batch;
+  a.out_logits = out;
+  a.n_kept = n_kept;
+  a.vocab = vocab;
+  a.ws = static_cast<uint8_t*>(ws);
+  return status(launch_gemv(a, static_cast<hipStream_t>(stream)));
+}
+
+// Checks shared by the quantizers.
+static int check_quant(const void* w, int64_t vocab, int64_t hidden,
+                       const int32_t* ids, int64_t n_rows, const void* out,
+                       uintptr_t out_align, const float* scale,
+                       const void* ws, size_t ws_bytes) {
+  if (!w || !ids || !out || !scale) return DH_EINVAL;
+  if (vocab < 1 || vocab > INT32_MAX || n_rows < 1 || n_rows > INT32_MAX)
+    return DH_EINVAL;
+  if (hidden < 16 || hidden > 16384 || hidden % 16 != 0) return DH_EINVAL;
+  if (!aligned(w, 16) || !aligned(out, out_align) || !aligned(ids, 4) ||
+      !aligned(scale, 4))
+    return DH_EINVAL;
+  if (!ws || !aligned(ws, 16) || ws_bytes < workspace_bytes(n_rows, 1))
     return DH_EWORKSPACE;
   return DH_OK;
 }
@@ -106,17 +180,11 @@ int nvfp4_quantize_rows(const void* w_bf16, int64_t vocab, int64_t hidden,
                         uint8_t* packed, uint8_t* scales, float* global_scale,
                         void* workspace, size_t workspace_bytes,
                         void* stream) {
-  if (!w_bf16 || !row_ids || !packed || !scales || !global_scale)
-    return DH_EINVAL;
-  if (vocab < 1 || vocab > INT32_MAX || n_rows < 1 || n_rows > INT32_MAX)
-    return DH_EINVAL;
-  if (hidden < 16 || hidden > 16384 || hidden % 16 != 0) return DH_EINVAL;
-  if (!dh::aligned(w_bf16, 16) || !dh::aligned(packed, 8) ||
-      !dh::aligned(row_ids, 4) || !dh::aligned(global_scale, 4))
-    return DH_EINVAL;
-  if (!workspace || !dh::aligned(workspace, 16) ||
-      workspace_bytes < dh::workspace_bytes(n_rows, 1))
-    return DH_EWORKSPACE;
+  if (!scales) return DH_EINVAL;
+  const int rc = dh::check_quant(w_bf16, vocab, hidden, row_ids, n_rows,
+                                 packed, 8, global_scale, workspace,
+                                 workspace_bytes);
+  if (rc != DH_OK) return rc;
   dh::QuantArgs a;
   a.w = static_cast<const uint16_t*>(w_bf16);
   a.vocab = vocab;
@@ -131,28 +199,35 @@ int nvfp4_quantize_rows(const void* w_bf16, int64_t vocab, int64_t hidden,
       dh::launch_nvfp4_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
+int e4m3_quantize_rows_per_tensor(const void* w_bf16, int64_t vocab,
+                                  int64_t hidden, const int32_t* row_ids,
+                                  int64_t n_rows, uint8_t* q, float* scale,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const int rc = dh::check_quant(w_bf16, vocab, hidden, row_ids, n_rows, q, 8,
+                                 scale, workspace, workspace_bytes);
+  if (rc != DH_OK) return rc;
+  dh::QuantE4m3Args a;
+  a.w = static_cast<const uint16_t*>(w_bf16);
+  a.vocab = vocab;
+  a.hidden = hidden;
+  a.ids = row_ids;
+  a.n_rows = n_rows;
+  a.q = q;
+  a.scale = scale;
+  a.ws = static_cast<uint8_t*>(workspace);
+  return dh::status(
+      dh::launch_e4m3_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
 int draft_head_top_tokens(const uint8_t* packed, const uint8_t* scales,
                           const float* global_scale, const int32_t* dh_idx,
                           int64_t n_rows, int64_t hidden, const void* h_bf16,
                           int64_t batch, int32_t* out_ids, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  if (!out_ids || !dh::aligned(out_ids, 4)) return DH_EINVAL;
-  int rc = dh::check_head(packed, scales, global_scale, dh_idx, n_rows, hidden,
-                          h_bf16, batch, workspace, workspace_bytes);
-  if (rc != DH_OK) return rc;
-  dh::GemvArgs a{};
-  a.packed = packed;
-  a.scales = scales;
-  a.global_scale = global_scale;
-  a.dh_idx = dh_idx;
-  a.n_rows = n_rows;
-  a.hidden = hidden;
-  a.h = static_cast<const uint16_t*>(h_bf16);
-  a.batch = batch;
-  a.out_ids = out_ids;
-  a.ws = static_cast<uint8_t*>(workspace);
-  return dh::status(
-      dh::launch_nvfp4_top_tokens(a, static_cast<hipStream_t>(stream)));
+  return dh::top_tokens(dh::FMT_NVFP4, packed, scales, global_scale, dh_idx,
+                        n_rows, hidden, h_bf16, batch, out_ids, workspace,
+                        workspace_bytes, stream);
 }
 
 int draft_head_logits(const uint8_t* packed, const uint8_t* scales,
@@ -161,27 +236,51 @@ int draft_head_logits(const uint8_t* packed, const uint8_t* scales,
                       int64_t vocab, const void* h_bf16, int64_t batch,
                       float* out_logits, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  if (!out_logits || !dh::aligned(out_logits, 16)) return DH_EINVAL;
-  if (n_kept < 1 || n_kept > n_rows || vocab < n_kept || vocab > INT32_MAX)
-    return DH_EINVAL;
-  int rc = dh::check_head(packed, scales, global_scale, dh_idx, n_rows, hidden,
-                          h_bf16, batch, workspace, workspace_bytes);
-  if (rc != DH_OK) return rc;
-  dh::GemvArgs a{};
-  a.packed = packed;
-  a.scales = scales;
-  a.global_scale = global_scale;
-  a.dh_idx = dh_idx;
-  a.n_rows = n_rows;
-  a.hidden = hidden;
-  a.h = static_cast<const uint16_t*>(h_bf16);
-  a.batch = batch;
-  a.out_logits = out_logits;
-  a.n_kept = n_kept;
-  a.vocab = vocab;
-  a.ws = static_cast<uint8_t*>(workspace);
-  return dh::status(
-      dh::launch_nvfp4_logits(a, static_cast<hipStream_t>(stream)));
+  return dh::logits(dh::FMT_NVFP4, packed, scales, global_scale, dh_idx,
+                    n_rows, n_kept, hidden, vocab, h_bf16, batch, out_logits,
+                    workspace, workspace_bytes, stream);
+}
+
+int draft_head_top_tokens_e4m3(const uint8_t* q, const float* scale,
+                               const int32_t* dh_idx, int64_t n_rows,
+                               int64_t hidden, const void* h_bf16,
+                               int64_t batch, int32_t* out_ids,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return dh::top_tokens(dh::FMT_E4M3, q, nullptr, scale, dh_idx, n_rows,
+                        hidden, h_bf16, batch, out_ids, workspace,
+                        workspace_bytes, stream);
+}
+
+int draft_head_logits_e4m3(const uint8_t* q, const float* scale,
+                           const int32_t* dh_idx, int64_t n_rows,
+                           int64_t n_kept, int64_t hidden, int64_t vocab,
+                           const void* h_bf16, int64_t batch,
+                           float* out_logits, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return dh::logits(dh::FMT_E4M3, q, nullptr, scale, dh_idx, n_rows, n_kept,
+                    hidden, vocab, h_bf16, batch, out_logits, workspace,
+                    workspace_bytes, stream);
+}
+
+int draft_head_top_tokens_bf16(const void* w_bf16, const int32_t* dh_idx,
+                               int64_t n_rows, int64_t hidden,
+                               const void* h_bf16, int64_t batch,
+                               int32_t* out_ids, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return dh::top_tokens(dh::FMT_BF16, w_bf16, nullptr, nullptr, dh_idx,
+                        n_rows, hidden, h_bf16, batch, out_ids, workspace,
+                        workspace_bytes, stream);
+}
+
+int draft_head_logits_bf16(const void* w_bf16, const int32_t* dh_idx,
+                           int64_t n_rows, int64_t n_kept, int64_t hidden,
+                           int64_t vocab, const void* h_bf16, int64_t batch,
+                           float* out_logits, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return dh::logits(dh::FMT_BF16, w_bf16, nullptr, nullptr, dh_idx, n_rows,
+                    n_kept, hidden, vocab, h_bf16, batch, out_logits,
+                    workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -15,7 +15,8 @@ namespace dh {
 //   WS_GROUP + g*WS_GSTEP arrival counter of block group g (g < ARRIVAL_GROUPS);
 //                         4 KB apart so that each sits in its own memory
 //                         channel: same-address atomics serialize
-//   WS_PARTIALS           uint64 (value, row) per block per batch row
+//   WS_PARTIALS           uint64 (value, row) per block per batch row of
+//                         a slice (at most MAX_SLICE)
 constexpr size_t WS_TOP = 0;
 constexpr size_t WS_AMAX = 64;
 constexpr int ARRIVAL_GROUPS = 32;
@@ -24,6 +25,7 @@ constexpr size_t WS_GROUP = WS_GSTEP;
 constexpr size_t WS_PARTIALS = WS_GROUP + ARRIVAL_GROUPS * WS_GSTEP;
 constexpr int MAX_GRID = 4096;  // upper bound of any argmax grid
 constexpr int MAX_BATCH = 64;
+constexpr int MAX_SLICE = 16;   // batch rows per kernel launch
 
 size_t workspace_bytes(int64_t n_rows, int64_t batch);
 
@@ -46,22 +48,33 @@ struct QuantArgs {
 };
 hipError_t launch_nvfp4_quantize(const QuantArgs& a, hipStream_t s);
 
+struct QuantE4m3Args {
+  const uint16_t* w;
+  int64_t vocab, hidden;
+  const int32_t* ids;
+  int64_t n_rows;
+  uint8_t* q;
+  float* scale;
+  uint8_t* ws;
+};
+hipError_t launch_e4m3_quantize(const QuantE4m3Args& a, hipStream_t s);
+
+// One GEMV call: weight format (WeightFormat in formats.h), the head, h and
+// either out_ids (top tokens) or out_logits (logits scatter).
 struct GemvArgs {
-  const uint8_t* packed;
-  const uint8_t* scales;
-  const float* global_scale;
+  int fmt;
+  const uint8_t* w;       // NVFP4 packed codes, E4M3 bytes or BF16 rows
+  const uint8_t* scales;  // NVFP4 block scales, else null
+  const float* scale;     // NVFP4 global / E4M3 tensor scale; null for BF16
   const int32_t* dh_idx;
   int64_t n_rows, hidden;
   const uint16_t* h;
   int64_t batch;
-  // top-token mode
-  int32_t* out_ids;
-  // logits mode (out_logits != nullptr)
-  float* out_logits;
+  int32_t* out_ids;   // top-token mode
+  float* out_logits;  // logits mode when non-null
   int64_t n_kept, vocab;
   uint8_t* ws;
 };
-hipError_t launch_nvfp4_top_tokens(const GemvArgs& a, hipStream_t s);
-hipError_t launch_nvfp4_logits(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
 
 }  // namespace dh

@@ -1,0 +1,119 @@
+// Launch planning of the GEMV calls: the batch is cut into slices, each slice
+// goes to the batch-1 stream kernel (one row, a hidden size it has a shape
+// for), the MFMA kernel (two or more rows, hidden a multiple of four
+// chunks, h fits LDS) or the generic kernel, and the grid is sized to one
+// resident wave of blocks (never more blocks than work units).  The logits
+// path first fills the output with -inf (page 1, "q38_draft.py",
+// compute_logits: ids that were not kept score -inf).
+#include "gemv_common.h"
+
+namespace dh {
+namespace {
+
+constexpr int FILL_THREADS = 256;
+constexpr int GENERIC_LDS = 64 * 1024;
+
+__global__ __launch_bounds__(FILL_THREADS) void k_fill_neg_inf(float* out,
+                                                               int64_t n) {
+  const int64_t n4 = n / 4;
+  float4* o4 = reinterpret_cast<float4*>(out);
+  const float ninf = -INFINITY;
+  const int64_t stride = (int64_t)gridDim.x * FILL_THREADS;
+  for (int64_t i = (int64_t)blockIdx.x * FILL_THREADS + threadIdx.x; i < n4;
+       i += stride)
+    o4[i] = make_float4(ninf, ninf, ninf, ninf);
+  for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * FILL_THREADS + threadIdx.x;
+       i < n; i += stride)
+    out[i] = ninf;
+}
+
+// Largest generic slice in {8,4,2,1} that fits the remaining rows and LDS.
+int generic_slice(int64_t remaining, int64_t hidden) {
+  for (int bc = 8; bc > 1; bc >>= 1)
+    if (bc <= remaining && (int64_t)bc * hidden * 2 <= GENERIC_LDS) return bc;
+  return 1;
+}
+
+hipError_t plan_slice(const GemvArgs& ga, int64_t remaining,
+                      const DeviceInfo& di, KernelDesc* d, int* bc) {
+  const bool logits = ga.out_logits != nullptr;
+  if (remaining == 1 && b1_kernel(ga.fmt, ga.hidden, logits, d)) {
+    *bc = 1;
+    return hipSuccess;
+  }
+  if (remaining >= 2) {
+    int nb = mfma_max_slice(ga.hidden, di.lds_per_block);
+    if (nb > remaining) nb = (int)remaining;
+    if (nb >= 2 &&
+        mfma_kernel(ga.fmt, ga.hidden, nb, logits, di.lds_per_block, d)) {
+      *bc = nb;
+      return hipSuccess;
+    }
+  }
+  *bc = generic_slice(remaining, ga.hidden);
+  return generic_kernel(ga.fmt, *bc, ga.hidden, logits, d)
+             ? hipSuccess
+             : hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const bool logits = ga.out_logits != nullptr;
+  if (logits) {
+    const int64_t n = ga.batch * ga.vocab;
+    int64_t blocks = (n / 4 + FILL_THREADS - 1) / FILL_THREADS;
+    if (blocks > (int64_t)di.cus * 8) blocks = (int64_t)di.cus * 8;
+    if (blocks < 1) blocks = 1;
+    k_fill_neg_inf<<<(int)blocks, FILL_THREADS, 0, s>>>(ga.out_logits, n);
+  }
+  for (int64_t b0 = 0; b0 < ga.batch;) {
+    KernelDesc d;
+    int bc = 0;
+    e = plan_slice(ga, ga.batch - b0, di, &d, &bc);
+    if (e != hipSuccess) return e;
+    if (d.lds_bytes > 64 * 1024) {
+      e = hipFuncSetAttribute(d.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)d.lds_bytes);
+      if (e != hipSuccess) return e;
+    }
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, d.fn, d.threads,
+                                                     d.lds_bytes);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    const int waves = d.threads / 64;
+    const int64_t units = ga.n_rows / d.rows_per_unit;
+    int64_t grid = (int64_t)di.cus * occ;
+    const int64_t by_work = (units + waves - 1) / waves;
+    if (grid > by_work) grid = by_work;
+    if (grid > MAX_GRID) grid = MAX_GRID;
+    if (grid < 1) grid = 1;
+    KArgs k;
+    k.w = ga.w;
+    k.scales = ga.scales;
+    k.scale = ga.scale;
+    k.dh_idx = ga.dh_idx;
+    k.n_rows = ga.n_rows;
+    k.hidden = ga.hidden;
+    k.h = ga.h + b0 * ga.hidden;
+    k.nb = bc;
+    k.out_ids = logits ? nullptr : ga.out_ids + b0;
+    k.out_logits = logits ? ga.out_logits + b0 * ga.vocab : nullptr;
+    k.n_kept = ga.n_kept;
+    k.vocab = ga.vocab;
+    k.ws = ga.ws;
+    void* kargs[] = {&k};
+    e = hipLaunchKernel(d.fn, dim3((unsigned)grid), dim3(d.threads), kargs,
+                        d.lds_bytes, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    b0 += bc;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dh

@@ -1,0 +1,100 @@
+// GEMV for every shape the batch-1 and MFMA kernels do not cover (any
+// hidden % 16 == 0, batch slices of 1, 2, 4 or 8 rows): one head row per wave
+// iteration, 8-byte units (one NVFP4 block, 8 E4M3 or 4 BF16 elements)
+// strided over the 64 lanes, h of every batch row of the slice in LDS.
+// Computes what gemv_common.h states; fused with the argmax or the logits
+// scatter.
+#include "gemv_common.h"
+
+namespace dh {
+namespace {
+
+constexpr int THREADS = 256;
+
+template <class F, int B, bool LOGITS>
+__global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
+  constexpr int NW = THREADS / 64;
+  constexpr int HD = F::EPU / 2;  // h dwords per unit
+  extern __shared__ uint4 hs4[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.h);
+    const int n = (int)(B * a.hidden / 8);
+    for (int t = threadIdx.x; t < n; t += THREADS) hs4[t] = src[t];
+    __syncthreads();
+  }
+  const uint32_t* hs = reinterpret_cast<const uint32_t*>(hs4);
+  const float sc = LOGITS ? tensor_scale(a) : 1.0f;
+  float best_v[B];
+  int best_r[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    best_v[b] = -INFINITY;
+    best_r[b] = INT_MAX;
+  }
+  const int64_t nu = a.hidden / F::EPU;  // units per row
+  const int64_t r0 = (int64_t)blockIdx.x * a.n_rows / gridDim.x;
+  const int64_t r1 = (int64_t)(blockIdx.x + 1) * a.n_rows / gridDim.x;
+  for (int64_t row = r0 + wave; row < r1; row += NW) {
+    const uint2* prow = reinterpret_cast<const uint2*>(a.w) + row * nu;
+    const uint8_t* srow = a.scales + row * nu;  // NVFP4: one scale per unit
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    for (int64_t c = lane; c < nu; c += 64) {
+      const uint2 p = prow[c];
+      const uint32_t s = F::SCALED ? (uint32_t)srow[c] : 0u;
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        acc[b] = F::unit_dot(p, s, hs + b * (a.hidden / 2) + c * HD, acc[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float v = group_sum<64>(acc[b]);
+      if constexpr (LOGITS) {
+        if (lane == 0 && row < a.n_kept)
+          a.out_logits[b * a.vocab + a.dh_idx[row]] = v * sc;
+      } else if (v > best_v[b]) {
+        best_v[b] = v;
+        best_r[b] = (int)row;
+      }
+    }
+  }
+  if constexpr (!LOGITS) argmax_finish<B, THREADS>(best_v, best_r, a);
+}
+
+template <class F, bool L>
+bool pick(int nb, KernelDesc* d) {
+  const void* fn = nullptr;
+  switch (nb) {
+    case 1: fn = reinterpret_cast<const void*>(k_generic<F, 1, L>); break;
+    case 2: fn = reinterpret_cast<const void*>(k_generic<F, 2, L>); break;
+    case 4: fn = reinterpret_cast<const void*>(k_generic<F, 4, L>); break;
+    case 8: fn = reinterpret_cast<const void*>(k_generic<F, 8, L>); break;
+    default: return false;
+  }
+  *d = KernelDesc{fn, THREADS, 1, 0};
+  return true;
+}
+
+template <class F>
+bool pick_fmt(int nb, int64_t hidden, bool logits, KernelDesc* d) {
+  if (hidden % F::EPU != 0) return false;
+  if (!(logits ? pick<F, true>(nb, d) : pick<F, false>(nb, d))) return false;
+  d->lds_bytes = (size_t)nb * (size_t)hidden * 2;
+  return true;
+}
+
+}  // namespace
+
+bool generic_kernel(int fmt, int nb, int64_t hidden, bool logits,
+                    KernelDesc* out) {
+  switch (fmt) {
+    case FMT_NVFP4: return pick_fmt<Nvfp4>(nb, hidden, logits, out);
+    case FMT_E4M3: return pick_fmt<E4m3>(nb, hidden, logits, out);
+    case FMT_BF16: return pick_fmt<Bf16>(nb, hidden, logits, out);
+  }
+  return false;
+}
+
+}  // namespace dh

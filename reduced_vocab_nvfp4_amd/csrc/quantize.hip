@@ -1,4 +1,5 @@
-// Gather + NVFP4 quantization of the kept head rows on the device.
+// Gather + quantization of the kept head rows on the device: NVFP4 (the
+// method's format) and per-tensor E4M3 (the FP8 head it is compared with).
 //
 // Recipe (page 3, "...MTP-NVFP4-h98k", "How it was built"): global scale
 // amax / (6*448), E4M3 block scales per 16 elements, e2m1 codes rounded to
@@ -17,6 +18,13 @@
 // Every float operation is a single IEEE binary32 operation with
 // round-to-nearest-even (no contraction, correctly rounded division), in the
 // order gs = max(amax,1e-12)/2688, s = bmax/(6*gs), q = x/(e4m3(s)*gs).
+//
+// Per-tensor E4M3 (page 2, "FP8 MTP draft stack for vLLM",
+// _fp8_convert_draft_head: one scale amax/448 for the whole head, elements
+// divided by it, clamped to +-448 and cast to e4m3fn): the same amax pass,
+// then k_e4m3_encode with one thread per 8 elements, scale =
+// max(amax,1e-12)/448, code = E4M3 of clamp(x/scale), sign kept (a negative
+// zero quotient gives 0x80).
 #include "dh_device.h"
 #include "dh_internal.h"
 
@@ -116,10 +124,46 @@ __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
   }
 }
 
+__device__ __forceinline__ float e4m3_scale_from(uint32_t amax_bits) {
+  float amax = __uint_as_float(amax_bits);
+  return fmaxf(amax, 1e-12f) / 448.0f;
+}
+
+__global__ __launch_bounds__(QTHREADS) void k_e4m3_encode(
+    const uint16_t* __restrict__ w, int64_t hidden,
+    const int32_t* __restrict__ ids, int64_t n_rows,
+    const uint32_t* __restrict__ amax_bits, uint8_t* __restrict__ q) {
+  const int64_t upr = hidden / 8;  // 16-byte input units per row
+  const int64_t total = n_rows * upr;
+  const float scale = e4m3_scale_from(*amax_bits);
+  for (int64_t u = (int64_t)blockIdx.x * QTHREADS + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * QTHREADS) {
+    const int64_t j = u / upr, k = u - j * upr;
+    const uint4 v =
+        *reinterpret_cast<const uint4*>(w + (int64_t)ids[j] * hidden + k * 8);
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bits = (x[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+      float t = bf16_to_f32(bits) / scale;
+      t = fminf(fmaxf(t, -448.0f), 448.0f);
+      const uint32_t code =
+          e4m3_encode_nonneg(fabsf(t)) | ((__float_as_uint(t) >> 31) << 7);
+      out[i >> 2] |= code << ((i & 3) * 8);
+    }
+    *reinterpret_cast<uint2*>(q + j * hidden + k * 8) =
+        make_uint2(out[0], out[1]);
+  }
+}
+
+// Writes the tensor scale (NVFP4 global scale or E4M3 scale) and returns the
+// amax slot to zero.
+template <bool E4M3>
 __global__ void k_quant_finish(uint32_t* __restrict__ amax_bits,
-                               float* __restrict__ global_scale) {
+                               float* __restrict__ scale) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
-    *global_scale = global_scale_from(*amax_bits);
+    *scale = E4M3 ? e4m3_scale_from(*amax_bits) : global_scale_from(*amax_bits);
     *amax_bits = 0u;
   }
 }
@@ -143,7 +187,21 @@ hipError_t launch_nvfp4_quantize(const QuantArgs& a, hipStream_t s) {
   k_nvfp4_encode<<<grid_for(a.n_rows * (a.hidden / 16), di.cus), QTHREADS, 0,
                    s>>>(a.w, a.hidden, a.ids, a.n_rows, amax, a.packed,
                         a.scales);
-  k_quant_finish<<<1, 64, 0, s>>>(amax, a.global_scale);
+  k_quant_finish<false><<<1, 64, 0, s>>>(amax, a.global_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_quantize(const QuantE4m3Args& a, hipStream_t s) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  uint32_t* amax = reinterpret_cast<uint32_t*>(a.ws + WS_AMAX);
+  const int grid = grid_for(a.n_rows * (a.hidden / 8), di.cus);
+  k_gather_amax<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
+                                          amax);
+  k_e4m3_encode<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
+                                          amax, a.q);
+  k_quant_finish<true><<<1, 64, 0, s>>>(amax, a.scale);
   return hipGetLastError();
 }
 

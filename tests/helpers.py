@@ -105,3 +105,14 @@ def check_top_tokens(got_ids, L: np.ndarray, idx: np.ndarray, n_kept: int,
             f"(logit {lmax}); gap {lmax - lg}")
         exceptions += 1
     return exceptions
+
+
+_WEIGHTS = {}
+
+
+def head_weight(vocab: int, hidden: int):
+    """The seeded BF16 head of this shape, drawn once per test session."""
+    if (vocab, hidden) not in _WEIGHTS:
+        from reduced_vocab_nvfp4_amd import workloads
+        _WEIGHTS[(vocab, hidden)] = workloads.head_weight(vocab, hidden)
+    return _WEIGHTS[(vocab, hidden)]

@@ -58,6 +58,11 @@ def test_build_index_edge_cases():
 
 def test_workspace_bytes():
     assert dh.draft_head_workspace_bytes(64064, 1) >= 256 + 8 * 1024
+    # a batch above one may run kernels with 16 partials per block
+    assert (dh.draft_head_workspace_bytes(64064, 2)
+            >= dh.draft_head_workspace_bytes(64064, 1) + 4096 * 15 * 8)
+    assert (dh.draft_head_workspace_bytes(64064, 64)
+            == dh.draft_head_workspace_bytes(64064, 2))
     assert dh.draft_head_workspace_bytes(0, 1) == 0
     assert dh.draft_head_workspace_bytes(64, 0) == 0
     assert dh.draft_head_workspace_bytes(64, 65) == 0
@@ -125,3 +130,67 @@ def test_top_tokens_and_logits_reject_bad_arguments_on_the_host():
     assert logits(n_kept=129) == dh.DH_EINVAL
     assert logits(vocab=50) == dh.DH_EINVAL
     assert logits(out=FAKE + 4) == dh.DH_EINVAL
+
+
+def test_e4m3_quantize_rejects_bad_arguments_on_the_host():
+    L = dh.lib()
+    ws = dh.draft_head_workspace_bytes(64, 1)
+    args = dict(w=FAKE, V=1000, H=256, ids=FAKE, n=64, q=FAKE, s=FAKE,
+                ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.e4m3_quantize_rows_per_tensor(a["w"], a["V"], a["H"],
+                                               a["ids"], a["n"], a["q"],
+                                               a["s"], a["ws"], a["wsb"], None)
+    for bad in (dict(w=None), dict(ids=None), dict(q=None), dict(s=None),
+                dict(H=24), dict(H=0), dict(H=16400), dict(n=0), dict(V=0),
+                dict(w=FAKE + 2), dict(q=FAKE + 4), dict(s=FAKE + 2)):
+        assert call(**bad) == dh.DH_EINVAL, bad
+    assert call(ws=None) == dh.DH_EWORKSPACE
+    assert call(wsb=ws - 1) == dh.DH_EWORKSPACE
+
+
+def test_e4m3_and_bf16_heads_reject_bad_arguments_on_the_host():
+    L = dh.lib()
+    ws = dh.draft_head_workspace_bytes(128, 8)
+    base = dict(w=FAKE, s=FAKE, idx=FAKE, n=128, H=256, h=FAKE, B=1, out=FAKE,
+                ws=FAKE, wsb=ws)
+
+    def e4_top(**kw):
+        a = {**base, **kw}
+        return L.draft_head_top_tokens_e4m3(a["w"], a["s"], a["idx"], a["n"],
+                                            a["H"], a["h"], a["B"], a["out"],
+                                            a["ws"], a["wsb"], None)
+
+    def e4_logits(n_kept=100, vocab=1000, **kw):
+        a = {**base, **kw}
+        return L.draft_head_logits_e4m3(a["w"], a["s"], a["idx"], a["n"],
+                                        n_kept, a["H"], vocab, a["h"], a["B"],
+                                        a["out"], a["ws"], a["wsb"], None)
+
+    def bf_top(**kw):
+        a = {**base, **kw}
+        return L.draft_head_top_tokens_bf16(a["w"], a["idx"], a["n"], a["H"],
+                                            a["h"], a["B"], a["out"], a["ws"],
+                                            a["wsb"], None)
+
+    def bf_logits(n_kept=100, vocab=1000, **kw):
+        a = {**base, **kw}
+        return L.draft_head_logits_bf16(a["w"], a["idx"], a["n"], n_kept,
+                                        a["H"], vocab, a["h"], a["B"],
+                                        a["out"], a["ws"], a["wsb"], None)
+    for f in (e4_top, e4_logits, bf_top, bf_logits):
+        for bad in (dict(w=None), dict(idx=None), dict(h=None),
+                    dict(out=None), dict(n=100), dict(n=0), dict(H=40),
+                    dict(H=0), dict(B=0), dict(B=65), dict(w=FAKE + 8),
+                    dict(h=FAKE + 4)):
+            assert f(**bad) == dh.DH_EINVAL, (f.__name__, bad)
+        assert f(ws=None) == dh.DH_EWORKSPACE
+        assert f(wsb=16) == dh.DH_EWORKSPACE
+    assert e4_top(s=None) == dh.DH_EINVAL   # the E4M3 head needs its scale
+    for f in (e4_logits, bf_logits):
+        assert f(n_kept=0) == dh.DH_EINVAL
+        assert f(n_kept=129) == dh.DH_EINVAL
+        assert f(vocab=50) == dh.DH_EINVAL
+        assert f(out=FAKE + 4) == dh.DH_EINVAL

@@ -34,7 +34,7 @@ class Head:
         self.vocab = vocab or w_.vocab
         self.hidden = hidden or w_.hidden
         say(f"[setup] {name}: V={self.vocab} H={self.hidden}")
-        self.w = _weight(self.vocab, self.hidden)
+        self.w = H.head_weight(self.vocab, self.hidden)
         self.w_bits = wl.bf16_bits(self.w)
         keep = wl.keep_mask(w_)
         self.idx_o, self.n_kept = oracle.build_index(keep)
@@ -55,13 +55,6 @@ class Head:
 
 
 _heads = {}
-_weights = {}
-
-
-def _weight(vocab, hidden):
-    if (vocab, hidden) not in _weights:
-        _weights[(vocab, hidden)] = wl.head_weight(vocab, hidden)
-    return _weights[(vocab, hidden)]
 
 
 def head(name):
