@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
 """Draft-head step benchmark on one MI355X.
 
-One step = one greedy draft-head call, the hot path of the method
-(page 1, "q38_draft.py", get_top_tokens; page 4, "Qwen3.8-27B-NVFP4-DGX-SPARK",
-why native MTP plateaus: the head GEMV dominates a draft step): a W4A16
-NVFP4 GEMV of a BF16 hidden state against the kept rows, the argmax over them
-and the id remap, all in one kernel launch.  The row index and the NVFP4
-quantization happen once, at load, outside the timed region.
+One step = one draft-head call, the hot path of the method (page 1,
+"q38_draft.py", get_top_tokens / compute_logits; page 4,
+"Qwen3.8-27B-NVFP4-DGX-SPARK", why native MTP plateaus: the head GEMV
+dominates a draft step): a GEMV of BF16 hidden states against the kept head
+rows fused with the argmax and the id remap (or with the fp32 logits
+scatter).  The row index and the quantization happen once, at load, outside
+the timed region (the quantizer is timed separately).
 
-Default workload: the Flash-Next-shaped head, 248 320 x 2560 BF16 target
-head, 64 026 kept ids padded to 64 064 rows, batch 1.  Inputs are seeded and
-synthetic (see reduced_vocab_nvfp4_amd/workloads.py).
+Workloads (reduced_vocab_nvfp4_amd/workloads.py; seeded synthetic inputs):
+  flash_next_64k   NVFP4 64 064 x 2560, batch 1, top token  (default)
+  h98k_b16         NVFP4 (or --format e4m3) 98 304 x 2560, batch 16
+  dense27b_64k_b8  NVFP4 64 064 x 5120, batch 8, fp32 logits to 248 320 ids
+  stock_bf16       BF16 248 320 x 2560 (every id), batch 1, top token
+  tiny             NVFP4 1024 x 256, batch 1 (launch-bound; correctness)
 
-The timed region streams from HBM: R copies of the quantized head rotate so
-that R x 92 MB exceeds twice the 256 MB Infinity Cache.  Timing: HIP events
-recorded on the launch stream before and after K back-to-back launches
+The timed region streams from HBM: R copies of the head rotate so that
+R x head bytes exceeds twice the 256 MB Infinity Cache.  Timing: HIP events
+recorded on the launch stream before and after K back-to-back calls
 (preceded by a short GPU sleep so the host enqueues ahead of the device);
 `value` is algorithmic bytes per step / GPU time per step.
 
@@ -42,17 +46,25 @@ METRIC = ("draft-head µs/step and HBM GB/s (% peak), NVFP4 64064x2560 "
           "GEMV+argmax, batch 1")
 HBM_PEAK_GBS = 8000.0
 INFINITY_CACHE = 256 << 20
+RTOL, ATOL = 1e-3, 1e-4
 
 
-def algorithmic_bytes(n_rows, hidden, batch, logits_vocab=0):
-    """Bytes a step must move: packed codes, E4M3 scales, h, the global
-    scale, the out ids (and the dh_idx / logits traffic on the logits
-    path)."""
-    b = n_rows * hidden // 2 + n_rows * hidden // 16 + batch * hidden * 2 + 4
-    if logits_vocab:
-        b += n_rows * 4 + batch * logits_vocab * 4
+def weight_bytes(fmt, n_rows, hidden):
+    return {"nvfp4": n_rows * hidden // 2 + n_rows * hidden // 16,
+            "e4m3": n_rows * hidden,
+            "bf16": n_rows * hidden * 2}[fmt]
+
+
+def algorithmic_bytes(fmt, n_rows, hidden, batch, op, vocab):
+    """Bytes a step must move: the head (codes and scales), h, the tensor
+    scale, then either the winning dh_idx entries and the out ids, or the
+    dh_idx column and the full fp32 logits."""
+    b = weight_bytes(fmt, n_rows, hidden) + batch * hidden * 2
+    b += 4 if fmt != "bf16" else 0
+    if op == "logits":
+        b += n_rows * 4 + batch * vocab * 4
     else:
-        b += 4 + batch * 4  # the winning dh_idx entry and the out ids
+        b += batch * 4 + batch * 4
     return b
 
 
@@ -65,48 +77,218 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_hash):
-    """HBM traffic per launch from committed rocprofv3 counter runs, only if
+def load_traffic(case, kernel_hash):
+    """HBM traffic per step from committed rocprofv3 counter runs, only if
     they were taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic_flash_next_64k.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{case}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_hash:
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("hbm_bytes_per_step")
 
 
-def cpu_baseline(head, h_list, budget_s=10.0):
-    """The oracle's top-token step (float64 GEMV over every row, argmax,
-    remap) on the host, repeated on full steps until budget_s elapse."""
+class Case:
+    """One workload in one format: the head on the GPU, a lean per-step
+    call (pointers resolved once: argument marshalling only) and the oracle's
+    version of the step."""
+
+    def __init__(self, config, fmt, op, dev, stream):
+        self.config, self.fmt = config, fmt
+        w_ = wl.WORKLOADS[config]
+        if fmt not in w_.formats:
+            raise SystemExit(f"workload {config} has no {fmt} head "
+                             f"(formats: {', '.join(w_.formats)})")
+        self.V, self.H, self.B = w_.vocab, w_.hidden, w_.batch
+        default_op = "logits" if w_.logits and w_.batch > 1 else "top"
+        self.op = op or default_op
+        self.name = config if fmt == w_.formats[0] else f"{config}_{fmt}"
+        if self.op != default_op:
+            self.name += f"_{self.op}"
+        t0 = time.perf_counter()
+        self.w = wl.head_weight(self.V, self.H)
+        keep = wl.keep_mask(w_)
+        idx, self.n_kept = dh.draft_head_build_index(keep)
+        self.idx = idx.numpy()
+        self.n_rows = idx.shape[0]
+        self.idx_gpu = idx.to(dev)
+        self.ws = dh.new_workspace(self.n_rows, self.B, dev)
+        w_gpu = self.w.to(dev)
+        self.quant_us = None
+        if fmt == "nvfp4":
+            packed, scales, self.scale = dh.nvfp4_quantize_rows(
+                w_gpu, self.idx_gpu, workspace=self.ws)
+            quant = lambda: dh.nvfp4_quantize_rows(  # noqa: E731
+                w_gpu, self.idx_gpu, packed=packed, scales=scales,
+                global_scale=self.scale, workspace=self.ws)
+            tensors = (packed, scales)
+        elif fmt == "e4m3":
+            q, self.scale = dh.e4m3_quantize_rows_per_tensor(
+                w_gpu, self.idx_gpu, workspace=self.ws)
+            quant = lambda: dh.e4m3_quantize_rows_per_tensor(  # noqa: E731
+                w_gpu, self.idx_gpu, q=q, scale=self.scale,
+                workspace=self.ws)
+            tensors = (q,)
+        else:
+            rows = w_gpu if w_.identity else \
+                w_gpu[self.idx_gpu.long()].contiguous()
+            self.scale, quant, tensors = None, None, (rows,)
+        torch.cuda.synchronize()
+        if quant is not None:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(5):
+                quant()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            self.quant_us = ev[0].elapsed_time(ev[1]) * 1000.0 / 5
+        del w_gpu, quant
+        self.head_bytes = weight_bytes(fmt, self.n_rows, self.H)
+        self.nbytes = algorithmic_bytes(fmt, self.n_rows, self.H, self.B,
+                                        self.op, self.V)
+        self.setup_s = time.perf_counter() - t0
+        self.tensors = tensors
+
+    def rotate(self, R):
+        self.R = R
+        self.heads = [self.tensors] + [tuple(t.clone() for t in self.tensors)
+                                       for _ in range(R - 1)]
+
+    def make_step(self, h_ptrs, out, stream):
+        L = dh.lib()
+        sp = int(stream.cuda_stream)
+        heads = [tuple(t.data_ptr() for t in hd) for hd in self.heads]
+        sc = self.scale.data_ptr() if self.scale is not None else None
+        idx_p, ws_p, ws_n = (self.idx_gpu.data_ptr(), self.ws.data_ptr(),
+                             self.ws.numel())
+        n, H, B, R, nh = self.n_rows, self.H, self.B, self.R, len(h_ptrs)
+        out_p = out.data_ptr()
+        fmt = self.fmt
+        if self.op == "logits":
+            stride = B * self.V * 4
+            nk, V = self.n_kept, self.V
+
+            if fmt == "nvfp4":
+                def lcall(hd, hp, o):
+                    return L.draft_head_logits(hd[0], hd[1], sc, idx_p, n, nk,
+                                               H, V, hp, B, o, ws_p, ws_n, sp)
+            elif fmt == "e4m3":
+                def lcall(hd, hp, o):
+                    return L.draft_head_logits_e4m3(hd[0], sc, idx_p, n, nk,
+                                                    H, V, hp, B, o, ws_p,
+                                                    ws_n, sp)
+            else:
+                def lcall(hd, hp, o):
+                    return L.draft_head_logits_bf16(hd[0], idx_p, n, nk, H, V,
+                                                    hp, B, o, ws_p, ws_n, sp)
+
+            def step(i):
+                rc = lcall(heads[i % R], h_ptrs[i % nh],
+                           out_p + stride * (i % 2))
+                if rc:
+                    raise dh.DraftHeadError(f"logits ({fmt})", rc)
+            return step
+        if fmt == "nvfp4":
+            def call(hd, hp, o):
+                return L.draft_head_top_tokens(hd[0], hd[1], sc, idx_p, n, H,
+                                               hp, B, o, ws_p, ws_n, sp)
+        elif fmt == "e4m3":
+            def call(hd, hp, o):
+                return L.draft_head_top_tokens_e4m3(hd[0], sc, idx_p, n, H,
+                                                    hp, B, o, ws_p, ws_n, sp)
+        else:
+            def call(hd, hp, o):
+                return L.draft_head_top_tokens_bf16(hd[0], idx_p, n, H, hp,
+                                                    B, o, ws_p, ws_n, sp)
+
+        def step(i):
+            rc = call(heads[i % R], h_ptrs[i % nh], out_p + 4 * B * i)
+            if rc:
+                raise dh.DraftHeadError(f"top tokens ({fmt})", rc)
+        return step
+
+    # ---- the oracle's step ------------------------------------------------
+    def oracle_setup(self):
+        import oracle
+        bits = wl.bf16_bits(self.w)
+        t0 = time.perf_counter()
+        if self.fmt == "nvfp4":
+            self.o_head = oracle.nvfp4_quantize(bits, self.idx)
+        elif self.fmt == "e4m3":
+            self.o_head = oracle.e4m3_tensor_quantize(bits, self.idx)
+        else:
+            self.o_head = bits
+        return time.perf_counter() - t0
+
+    def oracle_step(self, h):
+        import oracle
+        hb = wl.bf16_bits(h)
+        if self.fmt == "nvfp4":
+            L = oracle.nvfp4_logits(*self.o_head, hb)
+        elif self.fmt == "e4m3":
+            L = oracle.e4m3_tensor_logits(*self.o_head, hb)
+        else:
+            L = oracle.bf16_logits(self.o_head, self.idx, hb)
+        if self.op == "logits":
+            return L, oracle.logits_scatter(L, self.n_kept, self.idx, self.V)
+        return L, oracle.argmax_remap(L, self.idx)[1]
+
+
+def cpu_baseline(case, h_list, budget_s):
+    """The oracle's step (float64 GEMV over every row, then argmax + remap
+    or the logits scatter) on the host, repeated on full steps until
+    budget_s elapse (at least one step)."""
     import oracle
-    t0 = time.perf_counter()
-    op, os_, ogs = oracle.nvfp4_quantize(head["w_bits"], head["idx"])
-    t_quant = time.perf_counter() - t0
-    times = []
-    ids = []
+    t_quant = case.oracle_setup()
+    times, results = [], []
     t_start = time.perf_counter()
     i = 0
     while True:
         h = h_list[i % len(h_list)]
         t0 = time.perf_counter()
-        L = oracle.nvfp4_logits(op, os_, ogs, wl.bf16_bits(h))
-        _, idd = oracle.argmax_remap(L, head["idx"])
+        r = case.oracle_step(h)
         times.append(time.perf_counter() - t0)
-        ids.append((i % len(h_list), int(idd[0]), L))
+        if i < len(h_list):
+            results.append(r)
         i += 1
         if time.perf_counter() - t_start > budget_s or i >= 64:
             break
-    return {
-        "step_s": float(np.median(times)),
-        "steps": len(times),
-        "threads": oracle.num_threads(),
-        "quantize_s": t_quant,
-        "ids": ids,
-        "oracle_head": (op, os_, ogs),
-    }
+    return {"step_s": float(np.median(times)), "steps": len(times),
+            "threads": oracle.num_threads(), "quantize_s": t_quant,
+            "results": results}
+
+
+def check_top(ids, results, case, n_h):
+    """Ids of every timed step whose h the oracle ran, with the near-tie
+    rule: a different id passes when its oracle logit is within the logit
+    tolerance of the oracle's maximum."""
+    parity = {"checked_steps": 0, "mismatches": 0, "near_tie_exceptions": 0}
+    for hi, (Lo, want) in enumerate(results):
+        for b in range(case.B):
+            lmax = Lo[b].max()
+            for g in ids[hi::n_h, b]:  # every step that used this h
+                parity["checked_steps"] += 1
+                if int(g) == int(want[b]):
+                    continue
+                r = np.flatnonzero(case.idx[:case.n_kept] == g)
+                gap = lmax - Lo[b, r[0]] if r.size else np.inf
+                if gap <= ATOL + RTOL * abs(lmax):
+                    parity["near_tie_exceptions"] += 1
+                else:
+                    parity["mismatches"] += 1
+    return parity
+
+
+def check_logits(out, ref):
+    fin = np.isfinite(ref)
+    bad = int((np.isfinite(out) != fin).sum())
+    bad += int((out.view(np.uint32)[~fin] != 0xFF800000).sum())
+    err = np.abs(out[fin].astype(np.float64) - ref[fin])
+    bad += int((err > ATOL + RTOL * np.abs(ref[fin])).sum())
+    return {"checked_values": int(out.size), "mismatches": bad,
+            "max_abs_err": float(err.max()) if err.size else 0.0}
 
 
 def main():
@@ -116,6 +298,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="flash_next_64k",
                     choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--format", default=None,
+                    choices=["nvfp4", "e4m3", "bf16"],
+                    help="head format (default: the workload's first)")
+    ap.add_argument("--op", default=None, choices=["top", "logits"],
+                    help="step kind (default: logits for the batch-8 "
+                         "logits workload, else top tokens)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="head copies to rotate (0: enough for 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -127,86 +315,54 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU "
-              "path (the head is replicated per GPU; see DESIGN.md)",
-              file=sys.stderr)
+              "path (the head is replicated per GPU)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
-    w_ = wl.WORKLOADS[args.config]
-    if "nvfp4" not in w_.formats:
-        print(f"workload {args.config} has no NVFP4 head", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    V, H, B = w_.vocab, w_.hidden, w_.batch
-
-    # ---- setup (untimed): weights, index, quantization ------------------
-    t0 = time.perf_counter()
-    w = wl.head_weight(V, H)
-    keep = wl.keep_mask(w_)
-    idx, n_kept = dh.draft_head_build_index(keep)
-    n_rows = idx.shape[0]
-    w_gpu = w.to(dev)
-    idx_gpu = idx.to(dev)
-    ws = dh.new_workspace(n_rows, B, dev)
-    packed, scales, gs = dh.nvfp4_quantize_rows(w_gpu, idx_gpu, workspace=ws)
-    torch.cuda.synchronize()
-    # quantizer timing (load-time step), a few repetitions
-    qe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    qe[0].record(stream)
-    for _ in range(5):
-        dh.nvfp4_quantize_rows(w_gpu, idx_gpu, packed=packed, scales=scales,
-                               global_scale=gs, workspace=ws)
-    qe[1].record(stream)
-    torch.cuda.synchronize()
-    quant_us = qe[0].elapsed_time(qe[1]) * 1000.0 / 5
-    del w_gpu
-    setup_s = time.perf_counter() - t0
+    fmt = args.format or wl.WORKLOADS[args.config].formats[0]
+    case = Case(args.config, fmt, args.op, dev, stream)
+    B, H, V = case.B, case.H, case.V
 
     if args.calibrate_copy:
-        src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
+        src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8,
+                          device=dev)
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
-    head_bytes = n_rows * H // 2 + n_rows * H // 16
-    R = args.rotate or max(1, -(-2 * INFINITY_CACHE // head_bytes) + 1)
-    heads = [(packed, scales)] + [(packed.clone(), scales.clone())
-                                  for _ in range(R - 1)]
+    if args.rotate:
+        R = args.rotate
+    elif case.head_bytes >= 2 * INFINITY_CACHE:
+        R = 1
+    else:
+        # small heads are launch-bound: a few copies are enough
+        R = min(16, -(-2 * INFINITY_CACHE // case.head_bytes) + 1)
+    case.rotate(R)
     n_h = 8
     h_cpu = [wl.hidden_states(B, H, s) for s in range(n_h)]
     h_gpu = [x.to(dev) for x in h_cpu]
+    h_ptrs = [x.data_ptr() for x in h_gpu]
     K, W = args.steps, args.warmup
-    out = torch.zeros((K + W, B), dtype=torch.int32, device=dev)
-
-    # Lean per-step call: pointers resolved once (argument marshalling only).
-    L = dh.lib()
-    sp = int(stream.cuda_stream)
-    heads_p = [(p.data_ptr(), s.data_ptr()) for p, s in heads]
-    h_p = [x.data_ptr() for x in h_gpu]
-    gs_p, idx_p, ws_p, ws_n = gs.data_ptr(), idx_gpu.data_ptr(), ws.data_ptr(), ws.numel()
-    out_p = out.data_ptr()
-
-    def step(i):
-        p, s = heads_p[i % R]
-        rc = L.draft_head_top_tokens(p, s, gs_p, idx_p, n_rows, H,
-                                     h_p[i % n_h], B, out_p + 4 * B * i,
-                                     ws_p, ws_n, sp)
-        if rc != 0:
-            raise dh.DraftHeadError("draft_head_top_tokens", rc)
-
+    if case.op == "logits":
+        out = torch.empty((2, B, V), dtype=torch.float32, device=dev)
+    else:
+        out = torch.zeros((K + W, B), dtype=torch.int32, device=dev)
+    step = case.make_step(h_ptrs, out, stream)
     for i in range(W):
-        step(K + i)
+        step(K + i if case.op == "top" else i)
     torch.cuda.synchronize()
 
-    # Timed region: K back-to-back launches between two events recorded on
-    # the launch stream (per-step event records would add their own gaps).
-    # A short device-side sleep first lets the host enqueue ahead of the GPU.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region: K back-to-back calls between two events recorded on the
+    # launch stream (per-step event records would add their own gaps).  A
+    # short device-side sleep first lets the host enqueue ahead of the GPU.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     try:
@@ -219,45 +375,33 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    total_us = e0.elapsed_time(e1) * 1000.0
-    us_step = total_us / K
+    us_step = e0.elapsed_time(e1) * 1000.0 / K
+    gbs = case.nbytes / (us_step * 1e-6) / 1e9
 
-    nbytes = algorithmic_bytes(n_rows, H, B)
-    gbs = nbytes / (us_step * 1e-6) / 1e9
-    ids = out[:K].cpu().numpy()
-
-    # ---- parity of sampled steps against the oracle, and the CPU leg ----
-    result_cpu = None
-    parity = {"checked_steps": 0, "mismatches": 0, "near_tie_exceptions": 0}
+    # ---- parity against the oracle, and the CPU leg -----------------------
+    result_cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cb = cpu_baseline({"w_bits": wl.bf16_bits(w), "idx": idx.numpy()},
-                          h_cpu, args.cpu_budget)
-        import oracle
-        idx_np = idx.numpy()
-        for hi, _, Lo in cb["ids"][:n_h]:
-            _, want = oracle.argmax_remap(Lo, idx_np)
-            for b in range(B):
-                lmax = Lo[b].max()
-                for g in ids[hi::n_h, b]:  # every step that used this h
-                    parity["checked_steps"] += 1
-                    if int(g) == int(want[b]):
-                        continue
-                    r = np.flatnonzero(idx_np[:n_kept] == g)
-                    gap = lmax - Lo[b, r[0]] if r.size else np.inf
-                    if gap <= 1e-4 + 1e-3 * abs(lmax):
-                        parity["near_tie_exceptions"] += 1
-                    else:
-                        parity["mismatches"] += 1
-        cpu_us = cb["step_s"] * 1e6
+        cb = cpu_baseline(case, h_cpu, args.cpu_budget)
+        if case.op == "logits":
+            # the last timed step used h[(K-1) % n_h] and buffer (K-1) % 2
+            hi = (K - 1) % n_h
+            ref = (cb["results"][hi] if hi < len(cb["results"])
+                   else case.oracle_step(h_cpu[hi]))[1]
+            parity = check_logits(out[(K - 1) % 2].cpu().numpy(), ref)
+        else:
+            parity = check_top(out[:K].cpu().numpy(), cb["results"], case,
+                               n_h)
+        what = "logits scatter" if case.op == "logits" else "argmax, remap"
         result_cpu = {
-            "value": round(nbytes / cb["step_s"] / 1e9, 3),
+            "value": round(case.nbytes / cb["step_s"] / 1e9, 3),
             "unit": "GB/s",
-            "us_per_step": round(cpu_us, 1),
+            "us_per_step": round(cb["step_s"] * 1e6, 1),
             "cores": cb["threads"],
             "kind": "oracle",
-            "sample": (f"{cb['steps']} full steps of {args.config} (float64 "
-                       f"GEMV over {n_rows} rows x {H}, argmax, remap), "
-                       f"median; host {os.cpu_count()} visible CPUs"),
+            "sample": (f"{cb['steps']} full steps of {case.name} (float64 "
+                       f"GEMV over {case.n_rows} rows x {H}, batch {B}, "
+                       f"{what}), median; host {os.cpu_count()} visible "
+                       f"CPUs"),
         }
 
     khash = kernel_source_hash()
@@ -276,8 +420,12 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": args.config, "vocab": V, "hidden": H, "batch": B,
-            "n_rows": n_rows, "n_kept": n_kept, "format": "nvfp4-w4a16",
+            "workload": case.name, "vocab": V, "hidden": H, "batch": B,
+            "n_rows": case.n_rows, "n_kept": case.n_kept,
+            "format": {"nvfp4": "nvfp4-w4a16", "e4m3": "e4m3-w8a16",
+                       "bf16": "bf16"}[fmt],
+            "step": ("top tokens" if case.op == "top" else
+                     "fp32 logits to the full vocab"),
             "rotated_head_copies": R, "parallelism": "none (1 GPU)",
         },
         "roofline": {
@@ -286,18 +434,19 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": load_traffic(khash),
-            "bytes_per_launch": nbytes,
+            "traffic": load_traffic(case.name, khash),
+            "bytes_per_step": case.nbytes,
+            "launches_per_step": 2 if case.op == "logits" else 1,
         },
         "cpu_baseline": result_cpu,
         "parity": parity,
-        "quantize_us": round(quant_us, 1),
-        "setup_s": round(setup_s, 1),
+        "quantize_us": round(case.quant_us, 1) if case.quant_us else None,
+        "setup_s": round(case.setup_s, 1),
         "wall_s_timed": round(t_wall, 4),
         "kernel_source_hash": khash,
     }
     print(json.dumps(rec), flush=True)
-    if parity["mismatches"]:
+    if parity and parity["mismatches"]:
         sys.exit(1)
 
 

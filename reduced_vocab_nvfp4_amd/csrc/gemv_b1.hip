@@ -195,7 +195,7 @@ bool desc(KernelDesc* d) {
   if constexpr (fits<F, G, C>()) {
     *d = KernelDesc{reinterpret_cast<const void*>(
                         k_b1<F, G, C, L, RING, B1_THREADS>),
-                    B1_THREADS, 64 / G, 0};
+                    B1_THREADS, 64 / G, 0, false};
     return true;
   }
   return false;

@@ -41,6 +41,7 @@ struct KernelDesc {
   int threads;
   int rows_per_unit;  // rows one wave owns per work unit
   size_t lds_bytes;   // dynamic LDS
+  bool spread;        // units dealt wave-major: one block per unit suffices
 };
 
 // Kernel families; each returns false when it has no kernel for the shape.
@@ -51,6 +52,11 @@ bool generic_kernel(int fmt, int nb, int64_t hidden, bool logits,
                     KernelDesc* out);
 // Largest batch slice the MFMA kernel can stage for this hidden size.
 int mfma_max_slice(int64_t hidden, int lds_per_block);
+// LDS bytes of one staged h row in the MFMA kernel: whole 1 KB pieces plus
+// 16 bytes of bank skew.
+__host__ __device__ inline int mfma_lds_row_bytes(int64_t hidden) {
+  return (int)((hidden * 2 + 1023) / 1024 * 1024 + 16);
+}
 
 __device__ __forceinline__ uint64_t pack_partial(float v, int r) {
   return ((uint64_t)(uint32_t)r << 32) | (uint64_t)__float_as_uint(v);
@@ -83,6 +89,8 @@ template <int B, int NT>
 __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
                                               int (&best_r)[B],
                                               const KArgs& a) {
+  static_assert(B >= 1 && B <= 64 && (B & (B - 1)) == 0 && NT % 64 == 0,
+                "batch slots are a power of two within a wave");
   constexpr int NW = NT / 64;
   __shared__ float sv[NW][B];
   __shared__ int sr[NW][B];
@@ -142,39 +150,61 @@ __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
   }
   __syncthreads();
   if (!is_last) return;
+  // Final pass over gridDim.x * B partials: thread t reads the partials of
+  // batch row t % B from blocks t / B, t / B + NT / B, ... (all its loads are
+  // issued before any is used), then lanes of the same batch row (B apart in
+  // a wave) and the waves combine.
+  constexpr int PER = NT / B;  // blocks one round covers
+  constexpr int UNR = 8;
+  const int bt = threadIdx.x % B;
+  float v = -INFINITY;
+  int r = INT_MAX;
+  for (int i0 = threadIdx.x / B; i0 < (int)gridDim.x; i0 += PER * UNR) {
+    uint64_t pv[UNR];
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    float v = -INFINITY;
-    int r = INT_MAX;
-    for (int i = threadIdx.x; i < (int)gridDim.x; i += NT) {
-      const uint64_t p = __hip_atomic_load(&part[(int64_t)i * B + b],
-                                           __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      const float pv = __uint_as_float((uint32_t)p);
-      const int pr = (int)(p >> 32);
-      if (better(pv, pr, v, r)) {
-        v = pv;
-        r = pr;
+    for (int u = 0; u < UNR; ++u) {
+      const int i = i0 + u * PER;
+      pv[u] = i < (int)gridDim.x
+                  ? __hip_atomic_load(&part[(int64_t)i * B + bt],
+                                      __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT)
+                  : pack_partial(-INFINITY, INT_MAX);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const float fv = __uint_as_float((uint32_t)pv[u]);
+      const int fr = (int)(pv[u] >> 32);
+      if (better(fv, fr, v, r)) {
+        v = fv;
+        r = fr;
       }
     }
-    wave_argmax(v, r);
-    if (lane == 0) {
-      sv[wave][b] = v;
-      sr[wave][b] = r;
+  }
+#pragma unroll
+  for (int off = B; off < 64; off <<= 1) {
+    const float ov = __shfl_xor(v, off, 64);
+    const int orow = __shfl_xor(r, off, 64);
+    if (better(ov, orow, v, r)) {
+      v = ov;
+      r = orow;
     }
+  }
+  if (lane < B) {
+    sv[wave][lane] = v;
+    sr[wave][lane] = r;
   }
   __syncthreads();
   if (threadIdx.x < B && threadIdx.x < a.nb) {
     const int b = threadIdx.x;
-    float v = sv[0][b];
-    int r = sr[0][b];
+    float fv = sv[0][b];
+    int fr = sr[0][b];
     for (int w = 1; w < NW; ++w)
-      if (better(sv[w][b], sr[w][b], v, r)) {
-        v = sv[w][b];
-        r = sr[w][b];
+      if (better(sv[w][b], sr[w][b], fv, fr)) {
+        fv = sv[w][b];
+        fr = sr[w][b];
       }
-    if (r < 0 || r >= a.n_rows) r = 0;  // only reachable with NaN inputs
-    a.out_ids[b] = a.dh_idx[r];
+    if (fr < 0 || fr >= a.n_rows) fr = 0;  // only reachable with NaN inputs
+    a.out_ids[b] = a.dh_idx[fr];
   }
 }
 

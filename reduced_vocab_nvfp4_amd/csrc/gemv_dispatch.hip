@@ -88,7 +88,7 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     const int waves = d.threads / 64;
     const int64_t units = ga.n_rows / d.rows_per_unit;
     int64_t grid = (int64_t)di.cus * occ;
-    const int64_t by_work = (units + waves - 1) / waves;
+    const int64_t by_work = d.spread ? units : (units + waves - 1) / waves;
     if (grid > by_work) grid = by_work;
     if (grid > MAX_GRID) grid = MAX_GRID;
     if (grid < 1) grid = 1;

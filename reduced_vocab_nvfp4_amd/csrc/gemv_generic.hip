@@ -73,7 +73,7 @@ bool pick(int nb, KernelDesc* d) {
     case 8: fn = reinterpret_cast<const void*>(k_generic<F, 8, L>); break;
     default: return false;
   }
-  *d = KernelDesc{fn, THREADS, 1, 0};
+  *d = KernelDesc{fn, THREADS, 1, 0, false};
   return true;
 }
 

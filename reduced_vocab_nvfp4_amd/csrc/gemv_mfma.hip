@@ -18,8 +18,10 @@
 // h at the matching k from LDS.  A chunk holds EPC/8 MFMA operands.
 //
 // Work: a wave owns units of RT row tiles (16 rows each) and walks the whole
-// hidden dimension for each unit, one chunk per lane per tile per step, with
-// a ring of NB register buffers (NB-1 steps of loads in flight).  h of the
+// hidden dimension for each unit, one chunk per lane per tile per step.  A
+// ring of NB register slots of SPS steps each keeps NB-1 slots of loads in
+// flight; the SPS loads of a tile are issued back to back so that DRAM sees
+// SPS*64 contiguous bytes of each row at once.  h of the
 // slice is staged once per block in LDS (row stride 2*hidden+16 bytes, so the
 // 16 batch rows of a read fall on different banks), plus one zero row that
 // the A-operand lanes of batch rows past the slice read.
@@ -28,42 +30,35 @@
 namespace dh {
 namespace {
 
-constexpr int MFMA_THREADS = 1024;
-constexpr int MFMA_RT = 2;  // 16-row tiles per work unit
-constexpr int MFMA_NB = 3;  // register buffers in the ring
-
-template <class F, int RT>
-struct Step {
-  uint4 p[RT];
-  uint32_t s[RT];
-};
-
-// Scalar cursor over (unit, step) pairs of one wave, with the row base of
-// the unit.
-struct Cursor {
-  int64_t row0;  // first row of the unit
-  int it;        // step within the unit
+// A work unit is RT 16-row tiles; a "slot" of the register ring holds SPS
+// consecutive steps of every tile, loaded back to back so that each head row
+// is read SPS*64 contiguous bytes at a time.
+template <class F, int RT, int SPS>
+struct Slot {
+  uint4 p[RT][SPS];
+  uint32_t s[RT][SPS];
+  int32_t ids[RT];  // dh_idx of the tile rows (logits path)
 };
 
 // The EPC/8 MFMAs of one step: operand O of every tile's chunk against the
 // h slots O of the lane's chunk.
-template <class F, int O, int RT>
-__device__ __forceinline__ void mfma_ops(const Step<F, RT>& b, const char* hp,
-                                         f32x4 (&acc)[RT]) {
+template <class F, int O, int RT, int SPS>
+__device__ __forceinline__ void mfma_ops(const Slot<F, RT, SPS>& b, int c,
+                                         const char* hp, f32x4 (&acc)[RT]) {
   if constexpr (O < F::EPC / 8) {
     const bf16x8 av = *reinterpret_cast<const bf16x8*>(hp + 16 * O);
 #pragma unroll
     for (int t = 0; t < RT; ++t)
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          av, F::template operand<O>(b.p[t], b.s[t]), acc[t], 0, 0, 0);
-    mfma_ops<F, O + 1, RT>(b, hp, acc);
+          av, F::template operand<O>(b.p[t][c], b.s[t][c]), acc[t], 0, 0, 0);
+    mfma_ops<F, O + 1, RT, SPS>(b, c, hp, acc);
   }
 }
 
-template <class F, int RT, int NB, bool LOGITS, int NT>
+template <class F, int RT, int SPS, int NB, bool LOGITS, int NT>
 __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   constexpr int NW = NT / 64;
-  constexpr int UR = 16 * RT;       // rows per unit
+  constexpr int UR = 16 * RT;  // rows per unit
   extern __shared__ uint4 hs[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q = lane >> 4;
@@ -71,31 +66,26 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   const int64_t hidden = a.hidden;
   const int nb = a.nb;
 
-  // Stage h [nb][hidden] and one zero row into LDS (row stride SB4 uint4).
-  const int64_t HU4 = hidden / 8;
-  const int64_t SB4 = HU4 + 1;
-  {
-    const uint4* h4 = reinterpret_cast<const uint4*>(a.h);
-    const int64_t tot = (int64_t)(nb + 1) * SB4;
-    for (int64_t i = threadIdx.x; i < tot; i += NT) {
-      const int64_t r = i / SB4, c = i - r * SB4;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nb && c < HU4) v = h4[r * HU4 + c];
-      hs[i] = v;
-    }
-  }
-  __syncthreads();
+  // h [nb][hidden] and one zero row are staged in LDS; a row takes whole
+  // 1 KB pieces plus 16 bytes (SB bytes), so the 16 batch rows of an A-operand
+  // read fall on different banks.
+  const int RBH = (int)(hidden * 2);  // h bytes per row
+  const int PPR = (RBH + 1023) / 1024;
+  const int SB = mfma_lds_row_bytes(hidden);
 
+  // Units are dealt wave-major (unit u goes to wave u / gridDim.x of block
+  // u % gridDim.x), so every block gets work even when there are fewer units
+  // than waves in the grid.
   const int64_t U = a.n_rows / UR;
   const int64_t TW = (int64_t)gridDim.x * NW;
-  const int64_t first = (int64_t)blockIdx.x * NW + wv;
+  const int64_t first = (int64_t)wv * gridDim.x + blockIdx.x;
   const int n_u = first < U ? (int)((U - first + TW - 1) / TW) : 0;
-  const int64_t CPR = hidden / F::EPC;  // 16-byte chunks per row
-  const int NI = (int)(CPR / 4);        // steps per unit
-  const int n_s = n_u * NI;
+  const int64_t CPR = hidden / F::EPC;    // 16-byte chunks per row
+  const int NS = (int)(CPR / (4 * SPS));  // slots per unit
+  const int n_s = n_u * NS;
   const int n_pad = (n_s + NB - 1) / NB * NB;
-  const int64_t RB = CPR * 16;          // weight bytes per row
-  const int64_t SPR = hidden / 16;      // scale bytes per row (NVFP4)
+  const int64_t RB = CPR * 16;      // weight bytes per row
+  const int64_t SPR = hidden / 16;  // scale bytes per row (NVFP4)
 
   // Per-lane constant parts of the addresses.
   uint32_t woff[RT], soff[RT];
@@ -107,27 +97,46 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   // A-operand LDS address of this lane at step 0: batch row min(m, nb)
   // (row nb is zero), chunk q.
   const int mrow = n < nb ? n : nb;
-  const uint32_t hoff = (uint32_t)(mrow * SB4 * 16 + q * F::EPC * 2);
+  const uint32_t hoff = (uint32_t)(mrow * SB + q * F::EPC * 2);
   const char* hsb = reinterpret_cast<const char*>(hs);
 
-  const Cursor start{(n_u > 0 ? first : 0) * UR, 0};
+  // Scalar cursor over (unit, slot) pairs: first row of the unit, slot.
+  int64_t ld_row0 = (n_u > 0 ? first : 0) * UR;
+  int ld_js = 0, ld_count = 0;
   const int64_t unit_stride = TW * UR;
-  auto advance = [&](Cursor& c) {
-    if (++c.it == NI) {
-      c.it = 0;
-      c.row0 += unit_stride;
-    }
-  };
-  auto load = [&](Step<F, RT>& b, const Cursor& c) {
-    const uint8_t* wb = a.w + c.row0 * RB + (int64_t)c.it * 64;
+  auto load = [&](Slot<F, RT, SPS>& b) {
+    // The cursor is passed through an opaque asm so that the compiler never
+    // folds the repeated loads of a clamped cursor into copies: the prologue
+    // wait below counts on every slot load being issued.
+    int64_t row0 = ld_row0;
+    int js = ld_js;
+    asm volatile("" : "+s"(row0), "+s"(js));
+    const uint8_t* wb = a.w + row0 * RB + (int64_t)js * (64 * SPS);
 #pragma unroll
     for (int t = 0; t < RT; ++t)
-      b.p[t] = *reinterpret_cast<const uint4*>(wb + woff[t]);
+#pragma unroll
+      for (int c = 0; c < SPS; ++c)
+        b.p[t][c] = *reinterpret_cast<const uint4*>(wb + woff[t] + 64 * c);
     if constexpr (F::SCALED) {
-      const uint8_t* sb = a.scales + c.row0 * SPR + (int64_t)c.it * 8;
+      const uint8_t* sb = a.scales + row0 * SPR + (int64_t)js * (8 * SPS);
 #pragma unroll
       for (int t = 0; t < RT; ++t)
-        b.s[t] = *reinterpret_cast<const uint16_t*>(sb + soff[t]);
+#pragma unroll
+        for (int c = 0; c < SPS; ++c)
+          b.s[t][c] = *reinterpret_cast<const uint16_t*>(sb + soff[t] + 8 * c);
+    }
+    if constexpr (LOGITS) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) b.ids[t] = a.dh_idx[row0 + 16 * t + n];
+    }
+    // The cursor stops at the wave's last slot: the surplus loads of the
+    // padded ring re-read it (L2 hits) and are never computed.
+    if (ld_count + 1 < n_s) {
+      ++ld_count;
+      if (++ld_js == NS) {
+        ld_js = 0;
+        ld_row0 += unit_stride;
+      }
     }
   };
 
@@ -143,43 +152,79 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
     best_r[j] = INT_MAX;
   }
 
-  // The load cursor stops at the wave's last step: the surplus loads of the
-  // padded ring re-read it (L2 hits) and are never computed.
-  Cursor ld = start;
-  int ld_count = 0;
-  auto advance_ld = [&]() {
-    if (ld_count + 1 < n_s) {
-      advance(ld);
-      ++ld_count;
+  // Prologue.  h goes straight into LDS with global_load_lds_dwordx4 (a
+  // wave copies 1 KB pieces: lane i's 16 bytes land at M0 + 16 i; lanes past
+  // the end of a row re-read its last 16 bytes into the row's padding), the
+  // zero row is written, and the first weight slots are issued, so the
+  // staging overlaps their latency.  Memory loads retire in issue order:
+  // once no more than the weight loads are outstanding, this wave's copies
+  // have landed; the barrier then covers every wave's.  (The copies are inline
+  // assembly with an explicit wait: the compiler does not order LDS reads
+  // after global_load_lds on its own, and a __syncthreads fence would also
+  // wait for the weight loads.)
+  {
+    const char* hb = reinterpret_cast<const char*>(a.h);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) void*)hs);
+    const int pieces = nb * PPR;
+    for (int pc = wv; pc < pieces; pc += NW) {
+      const int r = pc / PPR, j = pc - r * PPR;
+      const int off = j * 1024 + 16 * lane;
+      const int src = off < RBH ? off : RBH - 16;
+      asm volatile(
+          "s_mov_b32 m0, %1\n\t"
+          "global_load_lds_dwordx4 %0, off"
+          :
+          : "v"(hb + (int64_t)r * RBH + src),
+            "s"(lds_base + (uint32_t)(r * SB + j * 1024))
+          : "memory", "m0");
     }
-  };
-  Step<F, RT> buf[NB];
-#pragma unroll
-  for (int k = 0; k < NB - 1; ++k) {
-    load(buf[k], ld);
-    advance_ld();
+    uint4* zrow = hs + nb * (SB / 16);
+    for (int i = threadIdx.x; i < SB / 16; i += NT)
+      zrow[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  Cursor cp = start;
-  for (int s = 0; s < n_pad; s += NB) {
+  // Every wave has issued its copies before any wave issues weight loads:
+  // the CU's memory pipeline serves requests in order, so the copies (L2
+  // hits) do not queue behind the block's first HBM reads.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  Slot<F, RT, SPS> buf[NB];
+#pragma unroll
+  for (int k = 0; k < NB - 1; ++k) load(buf[k]);
+  constexpr int WEIGHT_LOADS =
+      (NB - 1) * (RT * SPS * (F::SCALED ? 2 : 1) + (LOGITS ? RT : 0));
+  static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(WEIGHT_LOADS)
+               : "memory");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  int64_t cp_row0 = (n_u > 0 ? first : 0) * UR;
+  int cp_js = 0;
+  for (int s0 = 0; s0 < n_pad; s0 += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      load(buf[(k + NB - 1) % NB], ld);
-      advance_ld();
+      load(buf[(k + NB - 1) % NB]);
       __builtin_amdgcn_sched_barrier(0);
-      if (s + k < n_s) {  // wave-uniform
-        mfma_ops<F, 0, RT>(buf[k], hsb + hoff + cp.it * (4 * F::EPC * 2), acc);
-        if (cp.it == NI - 1) {
+      if (s0 + k < n_s) {  // wave-uniform
+        const Slot<F, RT, SPS>& b = buf[k];
+#pragma unroll
+        for (int c = 0; c < SPS; ++c)
+          mfma_ops<F, 0, RT, SPS>(
+              b, c, hsb + hoff + (cp_js * SPS + c) * (4 * F::EPC * 2), acc);
+        if (cp_js == NS - 1) {
           // unit done: rows row0 + 16t + n, batch rows 4q + j
 #pragma unroll
           for (int t = 0; t < RT; ++t) {
-            const int64_t row = cp.row0 + 16 * t + n;
+            const int64_t row = cp_row0 + 16 * t + n;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float v = acc[t][j];
               if constexpr (LOGITS) {
                 const int m = 4 * q + j;
                 if (m < nb && row < a.n_kept)
-                  a.out_logits[(int64_t)m * a.vocab + a.dh_idx[row]] = v * sc;
+                  a.out_logits[(int64_t)m * a.vocab + b.ids[t]] = v * sc;
               } else if (v > best_v[j]) {
                 // a lane's rows ascend: strict > keeps the lowest
                 best_v[j] = v;
@@ -188,8 +233,11 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
             }
             acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           }
+          cp_js = 0;
+          cp_row0 += unit_stride;
+        } else {
+          ++cp_js;
         }
-        advance(cp);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -208,11 +256,29 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   }
 }
 
-template <class F, bool L>
+// Launch shape: one 16-row tile per unit, a double-buffered ring of slots of
+// up to ten steps (ten 1 KB loads per slot: 10-20 KB in flight per wave),
+// 512 threads per block (one block per CU: the h slice fills most of the LDS;
+// two waves per SIMD leave 256 VGPRs per wave for the ring).
+constexpr int MFMA_RT = 1;
+constexpr int MFMA_NB = 2;
+constexpr int MFMA_THREADS = 512;
+
+template <class F, int SPS, bool L>
 KernelDesc desc() {
   return KernelDesc{reinterpret_cast<const void*>(
-                        k_mfma<F, MFMA_RT, MFMA_NB, L, MFMA_THREADS>),
-                    MFMA_THREADS, 16 * MFMA_RT, 0};
+                        k_mfma<F, MFMA_RT, SPS, MFMA_NB, L, MFMA_THREADS>),
+                    MFMA_THREADS, 16 * MFMA_RT, 0, true};
+}
+
+// Steps per slot: the largest of 10, 4, 2, 1 that divides the steps of a
+// unit (hidden / (4 * EPC)).
+template <class F, bool L>
+KernelDesc desc_for(int64_t steps) {
+  if (steps % 10 == 0) return desc<F, 10, L>();
+  if (steps % 4 == 0) return desc<F, 4, L>();
+  if (steps % 2 == 0) return desc<F, 2, L>();
+  return desc<F, 1, L>();
 }
 
 template <class F>
@@ -220,15 +286,16 @@ bool pick(int64_t hidden, int nb, bool logits, int lds_per_block,
           KernelDesc* d) {
   if (hidden % (4 * F::EPC) != 0) return false;
   if (nb < 1 || nb > mfma_max_slice(hidden, lds_per_block)) return false;
-  *d = logits ? desc<F, true>() : desc<F, false>();
-  d->lds_bytes = (size_t)(nb + 1) * (size_t)(hidden * 2 + 16);
+  const int64_t steps = hidden / (4 * F::EPC);
+  *d = logits ? desc_for<F, true>(steps) : desc_for<F, false>(steps);
+  d->lds_bytes = (size_t)(nb + 1) * (size_t)mfma_lds_row_bytes(hidden);
   return true;
 }
 
 }  // namespace
 
 int mfma_max_slice(int64_t hidden, int lds_per_block) {
-  const int64_t row = hidden * 2 + 16;
+  const int64_t row = mfma_lds_row_bytes(hidden);
   int64_t nb = (int64_t)lds_per_block / row - 1;
   if (nb > 16) nb = 16;
   return nb < 0 ? 0 : (int)nb;
