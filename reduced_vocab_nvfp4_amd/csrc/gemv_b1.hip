@@ -22,24 +22,42 @@
 namespace dh {
 namespace {
 
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 template <class F, int C>
 struct Rows {
   uint4 p[C];
   uint32_t s[C];
 };
 
+// Loads the C chunks (and their scales) of one row group for this lane.
+// row0 is the group's first row (wave-uniform), lane_chunk = grp * CPR + g
+// the lane's first chunk within the group (loop-invariant): the address is a
+// scalar base plus a fixed per-lane offset, so no per-iteration address
+// registers are written while earlier loads are still outstanding.
 template <class F, int G, int C>
 __device__ __forceinline__ void load_rows(Rows<F, C>& r, const KArgs& a,
-                                          int64_t row, int g) {
+                                          int64_t row0, uint32_t lane_chunk) {
   constexpr int64_t CPR = (int64_t)G * C;  // chunks per row
-  const uint4* prow = reinterpret_cast<const uint4*>(a.w) + row * CPR;
+  // the group offset is made explicitly scalar, so the loads take the
+  // scalar-base + lane-offset form
+  const uint64_t woff = uniform_u64((uint64_t)row0 * (uint64_t)(CPR * 16));
+  const uint8_t* wb = a.w + woff;
 #pragma unroll
-  for (int i = 0; i < C; ++i) r.p[i] = prow[g + G * i];
+  for (int i = 0; i < C; ++i)
+    r.p[i] = *reinterpret_cast<const uint4*>(wb + 16u * (lane_chunk + G * i));
   if constexpr (F::SCALED) {
     // two E4M3 scales per chunk
-    const uint16_t* srow = reinterpret_cast<const uint16_t*>(a.scales) + row * CPR;
+    const uint8_t* sb = a.scales + (woff >> 3);
 #pragma unroll
-    for (int i = 0; i < C; ++i) r.s[i] = srow[g + G * i];
+    for (int i = 0; i < C; ++i)
+      r.s[i] =
+          *reinterpret_cast<const uint16_t*>(sb + 2u * (lane_chunk + G * i));
   }
 }
 
@@ -98,10 +116,11 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   const int n_pad = (n_it + NB - 1) / NB * NB;
   const int64_t base = n_it > 0 ? first : 0;
   const int last = n_it > 0 ? n_it - 1 : 0;
-  auto row_of = [&](int it) {
+  auto row0_of = [&](int it) {  // first row of the group (wave-uniform)
     const int c = it < last ? it : last;
-    return (base + (int64_t)c * TW) * R + grp;
+    return (base + (int64_t)c * TW) * R;
   };
+  const uint32_t lane_chunk = (uint32_t)(grp * G * C + g);
   // Prologue.  h is copied straight into this wave's LDS slice with
   // global_load_lds_dwordx4 (lane i's 16 bytes land at slice + 16*i; no
   // VGPRs, no block barrier), then the first weight row groups are issued,
@@ -130,7 +149,8 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   Rows<F, C> buf[NB];
 #pragma unroll
-  for (int k = 0; k < NB - 1; ++k) load_rows<F, G, C>(buf[k], a, row_of(k), g);
+  for (int k = 0; k < NB - 1; ++k)
+    load_rows<F, G, C>(buf[k], a, row0_of(k), lane_chunk);
   // Memory loads retire in issue order, so once no more than the weight
   // loads just issued are outstanding, the h copies have landed in LDS.
   // (The wait is explicit: the compiler does not order LDS reads after
@@ -161,11 +181,12 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
     for (int it = 0; it < n_pad; it += NB) {
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
-        load_rows<F, G, C>(buf[(k + NB - 1) % NB], a, row_of(it + k + NB - 1),
-                           g);
+        load_rows<F, G, C>(buf[(k + NB - 1) % NB], a, row0_of(it + k + NB - 1),
+                           lane_chunk);
         __builtin_amdgcn_sched_barrier(0);
         if (it + k < n_it)  // wave-uniform: padded iterations only load
-          compute_rows<F, G, C, LOGITS>(buf[k], a, row_of(it + k), g, hreg, sc,
+          compute_rows<F, G, C, LOGITS>(buf[k], a, row0_of(it + k) + grp, g,
+                                        hreg, sc,
                                         best_v, best_r);
         __builtin_amdgcn_sched_barrier(0);
       }
