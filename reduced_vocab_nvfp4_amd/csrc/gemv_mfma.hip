@@ -33,25 +33,70 @@ namespace {
 // A work unit is RT 16-row tiles; a "slot" of the register ring holds SPS
 // consecutive steps of every tile, loaded back to back so that each head row
 // is read SPS*64 contiguous bytes at a time.
+//
+// Block scales (NVFP4): step c of a slot needs the two scale bytes of chunk
+// 4c + q, 8 bytes apart from step to step.  With an even SPS the slot's
+// 8*SPS scale bytes of the lane's row are loaded as SPS/2 16-byte pieces
+// (the four lanes of a row load the same pieces) and each step picks its two
+// bytes out of them; an odd SPS loads them as one 16-bit value per step.
+template <class F, int SPS>
+constexpr bool wide_scales() {
+  return F::SCALED && SPS % 2 == 0;
+}
+
 template <class F, int RT, int SPS>
 struct Slot {
   uint4 p[RT][SPS];
-  uint32_t s[RT][SPS];
+  uint32_t s[RT][wide_scales<F, SPS>() ? 1 : SPS];
+  uint4 sw[RT][wide_scales<F, SPS>() ? SPS / 2 : 1];
   int32_t ids[RT];  // dh_idx of the tile rows (logits path)
 };
+
+// The two scale bytes of step C for a lane of k-slot group q.
+template <class F, int RT, int SPS, int C>
+__device__ __forceinline__ uint32_t slot_scale(const Slot<F, RT, SPS>& b,
+                                               int t, int q) {
+  if constexpr (wide_scales<F, SPS>()) {
+    // bytes 8C + 2q: dword 2C + q/2, half q%2
+    constexpr int D0 = 2 * C;
+    const uint4 lo = b.sw[t][D0 / 4];
+    const uint32_t w0 = (D0 % 4 == 0) ? lo.x : lo.z;
+    const uint32_t w1 = (D0 % 4 == 0) ? lo.y : lo.w;
+    const uint32_t w = (q & 2) ? w1 : w0;
+    return (q & 1) ? (w >> 16) : (w & 0xFFFFu);
+  } else if constexpr (F::SCALED) {
+    return b.s[t][C];
+  } else {
+    return 0u;
+  }
+}
 
 // The EPC/8 MFMAs of one step: operand O of every tile's chunk against the
 // h slots O of the lane's chunk.
 template <class F, int O, int RT, int SPS>
 __device__ __forceinline__ void mfma_ops(const Slot<F, RT, SPS>& b, int c,
+                                         const uint32_t (&sc)[RT],
                                          const char* hp, f32x4 (&acc)[RT]) {
   if constexpr (O < F::EPC / 8) {
     const bf16x8 av = *reinterpret_cast<const bf16x8*>(hp + 16 * O);
 #pragma unroll
     for (int t = 0; t < RT; ++t)
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          av, F::template operand<O>(b.p[t][c], b.s[t][c]), acc[t], 0, 0, 0);
-    mfma_ops<F, O + 1, RT, SPS>(b, c, hp, acc);
+          av, F::template operand<O>(b.p[t][c], sc[t]), acc[t], 0, 0, 0);
+    mfma_ops<F, O + 1, RT, SPS>(b, c, sc, hp, acc);
+  }
+}
+
+// The SPS steps of one slot.
+template <class F, int C, int RT, int SPS>
+__device__ __forceinline__ void slot_steps(const Slot<F, RT, SPS>& b, int q,
+                                           const char* hp, f32x4 (&acc)[RT]) {
+  if constexpr (C < SPS) {
+    uint32_t sc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) sc[t] = slot_scale<F, RT, SPS, C>(b, t, q);
+    mfma_ops<F, 0, RT, SPS>(b, C, sc, hp + C * (4 * F::EPC * 2), acc);
+    slot_steps<F, C + 1, RT, SPS>(b, q, hp, acc);
   }
 }
 
@@ -92,7 +137,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     woff[t] = (uint32_t)((16 * t + n) * RB + q * 16);
-    soff[t] = (uint32_t)((16 * t + n) * SPR + q * 2);
+    soff[t] = (uint32_t)((16 * t + n) * SPR +
+                         (wide_scales<F, SPS>() ? 0 : q * 2));
   }
   // A-operand LDS address of this lane at step 0: batch row min(m, nb)
   // (row nb is zero), chunk q.
@@ -123,7 +169,14 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
       for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int c = 0; c < SPS; ++c)
-          b.s[t][c] = *reinterpret_cast<const uint16_t*>(sb + soff[t] + 8 * c);
+          if constexpr (wide_scales<F, SPS>()) {
+            if (c < SPS / 2)
+              b.sw[t][c] =
+                  *reinterpret_cast<const uint4*>(sb + soff[t] + 16 * c);
+          } else {
+            b.s[t][c] =
+                *reinterpret_cast<const uint16_t*>(sb + soff[t] + 8 * c);
+          }
     }
     if constexpr (LOGITS) {
 #pragma unroll
@@ -192,8 +245,10 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   Slot<F, RT, SPS> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB - 1; ++k) load(buf[k]);
+  constexpr int SCALE_LOADS =
+      wide_scales<F, SPS>() ? SPS / 2 : (F::SCALED ? SPS : 0);
   constexpr int WEIGHT_LOADS =
-      (NB - 1) * (RT * SPS * (F::SCALED ? 2 : 1) + (LOGITS ? RT : 0));
+      (NB - 1) * (RT * (SPS + SCALE_LOADS) + (LOGITS ? RT : 0));
   static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(WEIGHT_LOADS)
@@ -209,10 +264,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if (s0 + k < n_s) {  // wave-uniform
         const Slot<F, RT, SPS>& b = buf[k];
-#pragma unroll
-        for (int c = 0; c < SPS; ++c)
-          mfma_ops<F, 0, RT, SPS>(
-              b, c, hsb + hoff + (cp_js * SPS + c) * (4 * F::EPC * 2), acc);
+        slot_steps<F, 0, RT, SPS>(
+            b, q, hsb + hoff + cp_js * SPS * (4 * F::EPC * 2), acc);
         if (cp_js == NS - 1) {
           // unit done: rows row0 + 16t + n, batch rows 4q + j
 #pragma unroll
@@ -287,7 +340,12 @@ bool pick(int64_t hidden, int nb, bool logits, int lds_per_block,
   if (hidden % (4 * F::EPC) != 0) return false;
   if (nb < 1 || nb > mfma_max_slice(hidden, lds_per_block)) return false;
   const int64_t steps = hidden / (4 * F::EPC);
-  *d = logits ? desc_for<F, true>(steps) : desc_for<F, false>(steps);
+  // 16-byte scale pieces need 16-byte aligned scale rows; otherwise one step
+  // per slot (the odd slot size loads the scales as 16-bit values)
+  if (F::SCALED && (hidden / 16) % 16 != 0)
+    *d = logits ? desc<F, 1, true>() : desc<F, 1, false>();
+  else
+    *d = logits ? desc_for<F, true>(steps) : desc_for<F, false>(steps);
   d->lds_bytes = (size_t)(nb + 1) * (size_t)mfma_lds_row_bytes(hidden);
   return true;
 }
