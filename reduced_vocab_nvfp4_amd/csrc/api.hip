@@ -18,7 +18,7 @@ size_t workspace_bytes(int64_t n_rows, int64_t batch) {
   // A batch of one runs the one-row kernels; any larger batch may run a
   // kernel that keeps MAX_SLICE partials per block.
   const int64_t slots = batch == 1 ? 1 : MAX_SLICE;
-  return WS_PARTIALS + (size_t)MAX_GRID * (size_t)slots * sizeof(uint64_t);
+  return WS_SLOTS + (size_t)MAX_GRID * (size_t)slots * 16;
 }
 
 hipError_t device_info(DeviceInfo* out) {

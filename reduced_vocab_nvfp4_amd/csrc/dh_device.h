@@ -108,11 +108,17 @@ __device__ __forceinline__ void argmax_step(float& v, int& r) {
   }
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int& r) {
+// (value, row) argmax within each 16-lane row: every lane ends with its
+// row's best.
+__device__ __forceinline__ void row_argmax(float& v, int& r) {
   argmax_step<DPP_QUAD_1032, 0xF>(v, r);
   argmax_step<DPP_QUAD_2301, 0xF>(v, r);
   argmax_step<DPP_ROW_HALF_MIRROR, 0xF>(v, r);
   argmax_step<DPP_ROW_MIRROR, 0xF>(v, r);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& r) {
+  row_argmax(v, r);
   argmax_step<DPP_ROW_BCAST15, 0xA>(v, r);
   argmax_step<DPP_ROW_BCAST31, 0xC>(v, r);
   v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));

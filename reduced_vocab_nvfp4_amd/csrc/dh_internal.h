@@ -8,21 +8,15 @@
 
 namespace dh {
 
-// Workspace layout (bytes).  The caller zero-fills it once; every kernel
-// that uses a slot returns it to zero before the call's work ends.
-//   WS_TOP                top-level arrival counter of the argmax finish
-//   WS_AMAX               amax bits of the quantizers
-//   WS_GROUP + g*WS_GSTEP arrival counter of block group g (g < ARRIVAL_GROUPS);
-//                         4 KB apart so that each sits in its own memory
-//                         channel: same-address atomics serialize
-//   WS_PARTIALS           uint64 (value, row) per block per batch row of
-//                         a slice (at most MAX_SLICE)
-constexpr size_t WS_TOP = 0;
+// Workspace layout (bytes).  The caller zero-fills it once; after that it
+// carries state from call to call and must not be modified between calls.
+//   WS_EPOCH   uint32 call counter of the argmax finish (tags its slots)
+//   WS_AMAX    amax bits of the quantizers, returned to zero by each call
+//   WS_SLOTS   16-byte tagged (value, row) slots, one per block per batch
+//              row of a slice (at most MAX_SLICE)
+constexpr size_t WS_EPOCH = 0;
 constexpr size_t WS_AMAX = 64;
-constexpr int ARRIVAL_GROUPS = 32;
-constexpr size_t WS_GSTEP = 4096;
-constexpr size_t WS_GROUP = WS_GSTEP;
-constexpr size_t WS_PARTIALS = WS_GROUP + ARRIVAL_GROUPS * WS_GSTEP;
+constexpr size_t WS_SLOTS = 256;
 constexpr int MAX_GRID = 4096;  // upper bound of any argmax grid
 constexpr int MAX_BATCH = 64;
 constexpr int MAX_SLICE = 16;   // batch rows per kernel launch

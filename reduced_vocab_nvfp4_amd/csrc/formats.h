@@ -26,6 +26,7 @@ namespace dh {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 enum WeightFormat : int { FMT_NVFP4 = 0, FMT_E4M3 = 1, FMT_BF16 = 2 };
 

@@ -48,9 +48,14 @@ __device__ __forceinline__ void load_rows(Rows<F, C>& r, const KArgs& a,
   // scalar-base + lane-offset form
   const uint64_t woff = uniform_u64((uint64_t)row0 * (uint64_t)(CPR * 16));
   const uint8_t* wb = a.w + woff;
+  // the head is read once per call: non-temporal loads keep it from
+  // displacing h and the scales in the caches
 #pragma unroll
-  for (int i = 0; i < C; ++i)
-    r.p[i] = *reinterpret_cast<const uint4*>(wb + 16u * (lane_chunk + G * i));
+  for (int i = 0; i < C; ++i) {
+    const u32x4 t = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(wb + 16u * (lane_chunk + G * i)));
+    r.p[i] = make_uint4(t[0], t[1], t[2], t[3]);
+  }
   if constexpr (F::SCALED) {
     // two E4M3 scales per chunk
     const uint8_t* sb = a.scales + (woff >> 3);
@@ -96,6 +101,7 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane / G, g = lane % G;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t epoch = LOGITS ? 0u : finish_epoch(a);
 
   // Row groups are dealt to the grid's waves round-robin (grid stride):
   // wave w of the grid takes groups w, w + TW, w + 2 TW, ...  The per-wave
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   if constexpr (!LOGITS) {
     float bv[1] = {best_v};
     int br[1] = {best_r};
-    argmax_finish<1, NT>(bv, br, a);
+    argmax_finish<1, NT>(bv, br, a, epoch);
   }
 }
 

@@ -66,46 +66,82 @@ __device__ __forceinline__ float tensor_scale(const KArgs& a) {
   return a.scale ? *a.scale : 1.0f;
 }
 
-// Block-level (value,row) reduction, the partial write and the last block's
-// final pass.  best_v/best_r are this lane's candidates for the B batch
-// columns of the slice (B = the slice's compile-time capacity; only the
-// first a.nb are written out).
+// Call counter of the argmax slots.  The workspace keeps it; a call's
+// blocks tag their slots with counter + 1 (0 is skipped: a zero-filled slot
+// is never valid) and the collecting block stores the tag back as the new
+// counter once it has read every slot.  The previous call's store is
+// visible to this one by stream order, and no block of this call reads the
+// counter after the collector writes it (every block reads it before it
+// publishes), so a plain load suffices.  Every wave issues it at the
+// kernel's start, unconditionally, and only the argmax finish uses the
+// value: its latency then hides behind the kernel's own work.  (It is an
+// atomic load only to keep the compiler from turning it into a scalar load,
+// whose wait would coincide with the first LDS wait.)
+__device__ __forceinline__ uint32_t finish_epoch(const KArgs& a) {
+  return __hip_atomic_load(reinterpret_cast<uint32_t*>(a.ws + WS_EPOCH),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Block-level (value,row) reduction, the partial write and the collection
+// of the partials.  best_v/best_r are this lane's candidates for the B batch columns of
+// the slice (B = the slice's compile-time capacity; only the first a.nb are
+// written out).  epoch = finish_epoch(a), loaded at the kernel's start (only
+// thread 0's value is used).
 //
-// Cross-block protocol.  Each block publishes its partials with agent-scope
-// atomic stores (performed at the device-coherent level, past the per-XCD
-// L2) and waits for them to complete (s_waitcnt vmcnt(0)) before it counts
-// its arrival.  Arrivals are counted in two levels: block b adds to the
-// counter of group b % ARRIVAL_GROUPS (counters 4 KB apart, in different
-// memory channels: same-address atomics serialize at ~10 ns each, so one
-// counter for the whole grid costs microseconds), the last arriver of a
-// group adds to the top counter, and the block that completes the top count
-// has seen every other block arrive after its partials were complete; it
-// reads them with agent-scope atomic loads.  This is the release/acquire
-// pairing restricted to the only locations that cross blocks; a general
-// agent-scope release fence would also write back the whole L2 in every
-// block, which costs tens of microseconds over a grid.  Every counter is
-// returned to zero by the block that completes it.
+// Cross-block protocol.  Every block publishes its (value, row) per batch
+// column in a slot of two 64-bit words, (tag, value bits) and (tag, row),
+// each written by an agent-scope atomic store (single-copy atomic, performed
+// past the per-XCD L2), and exits without waiting for them.  Block 0, after
+// its own share of the rows, polls the slots of column 0 with agent-scope
+// atomic loads until both words carry this call's tag; a slot can only hold
+// that tag once this call's owner wrote it, and the values travel inside
+// the atomics, so relaxed ordering suffices.  (Batch columns past the first
+// are collected the same way by blocks 1, 2, ...)  A collector learns of the last slot
+// about one memory round trip after it lands, where counting arrivals costs
+// a completion wait and an atomic round trip per counter level.  While it
+// polls, a collector also fetches dh_idx of each running best row, so the
+// winner's id is usually in hand when the last slot arrives.
+//
+// The wait is bounded: after FINISH_SPIN_LIMIT empty polls (seconds) a
+// collector gives up and writes -1 for its batch row.  No block waits on a
+// block that is not running: the collectors only wait for slots, and every
+// other block publishes without waiting, so the grid drains whatever the
+// dispatch order.
+constexpr int FINISH_SPIN_LIMIT = 1 << 22;
+
+struct FinishSlot {
+  uint64_t tv;  // tag << 32 | value bits
+  uint64_t tr;  // tag << 32 | row
+};
+
+// Per-wave candidates of a block, one per batch column, in LDS.
 template <int B, int NT>
-__device__ __forceinline__ void argmax_finish(float (&best_v)[B],
-                                              int (&best_r)[B],
-                                              const KArgs& a) {
-  static_assert(B >= 1 && B <= 64 && (B & (B - 1)) == 0 && NT % 64 == 0,
-                "batch slots are a power of two within a wave");
+struct WaveBest {
+  float v[NT / 64][B];
+  int r[NT / 64][B];
+};
+
+// The block's part once every wave has put its per-column best in w.
+template <int B, int NT>
+__device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
+                                                  const KArgs& a,
+                                                  uint32_t epoch) {
+  static_assert(B >= 1 && B <= 64 && NT % 64 == 0, "columns within a wave");
   constexpr int NW = NT / 64;
-  __shared__ float sv[NW][B];
-  __shared__ int sr[NW][B];
-  __shared__ int is_last;
+  const float(&sv)[NW][B] = w.v;
+  const int(&sr)[NW][B] = w.r;
+  __shared__ float cv[NW];  // collection: per-wave best of one column
+  __shared__ int cr[NW];
+  __shared__ int failed;
+  __shared__ uint32_t block_tag;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t* part = reinterpret_cast<uint64_t*>(a.ws + WS_PARTIALS);
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    wave_argmax(best_v[b], best_r[b]);
-    if (lane == 0) {
-      sv[wave][b] = best_v[b];
-      sr[wave][b] = best_r[b];
-    }
+  FinishSlot* slot = reinterpret_cast<FinishSlot*>(a.ws + WS_SLOTS);
+  if (threadIdx.x == 0) {
+    failed = 0;
+    block_tag = epoch + 1 == 0 ? 1u : epoch + 1;
   }
   __syncthreads();
+  const uint32_t tg = block_tag;
   if (threadIdx.x < B) {
     const int b = threadIdx.x;
     float v = sv[0][b];
@@ -115,97 +151,140 @@ __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
         v = sv[w][b];
         r = sr[w][b];
       }
-    __hip_atomic_store(&part[(int64_t)blockIdx.x * B + b], pack_partial(v, r),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = (uint64_t)tg << 32;
+    FinishSlot* s = slot + (int64_t)blockIdx.x * B + b;
+    __hip_atomic_store(&s->tv, hi | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&s->tr, hi | (uint32_t)r, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (threadIdx.x < 64) {
-    // all partial stores of the block come from wave 0 (B <= 64)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  }
-  if (threadIdx.x == 0) {
-    const uint32_t nblk = gridDim.x;
-    const uint32_t ng = nblk < ARRIVAL_GROUPS ? nblk : ARRIVAL_GROUPS;
-    const uint32_t grp = blockIdx.x % ARRIVAL_GROUPS;
-    const uint32_t gsize = (nblk - grp + ARRIVAL_GROUPS - 1) / ARRIVAL_GROUPS;
-    uint32_t* gcount =
-        reinterpret_cast<uint32_t*>(a.ws + WS_GROUP + grp * WS_GSTEP);
-    uint32_t* top = reinterpret_cast<uint32_t*>(a.ws + WS_TOP);
-    int last = 0;
-    const uint32_t t = __hip_atomic_fetch_add(gcount, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    if (t == gsize - 1) {
-      __hip_atomic_store(gcount, 0u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t u = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      if (u == ng - 1) {
-        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        last = 1;
-      }
-    }
-    is_last = last;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  // Final pass over gridDim.x * B partials: thread t reads the partials of
-  // batch row t % B from blocks t / B, t / B + NT / B, ... (all its loads are
-  // issued before any is used), then lanes of the same batch row (B apart in
-  // a wave) and the waves combine.
-  constexpr int PER = NT / B;  // blocks one round covers
+  // Collection.  Batch column b < min(nb, B) is collected by block
+  // b % gridDim.x, so the columns of a wide slice are polled from different
+  // CUs (the uncached polling loads of one CU are served one after another).
+  // Thread t polls the slots of blocks t + k * NT, UNR of them per round,
+  // and re-reads only those still pending.
+  const int nblk = (int)gridDim.x;
+  const int ncol = a.nb < B ? a.nb : B;
   constexpr int UNR = 8;
-  const int bt = threadIdx.x % B;
-  float v = -INFINITY;
-  int r = INT_MAX;
-  for (int i0 = threadIdx.x / B; i0 < (int)gridDim.x; i0 += PER * UNR) {
-    uint64_t pv[UNR];
+  for (int b = blockIdx.x; b < ncol; b += nblk) {
+    float v = -INFINITY;
+    int r = INT_MAX;
+    int id = 0;  // dh_idx[r] once r is a row
+    for (int i0 = threadIdx.x; i0 < nblk; i0 += NT * UNR) {
+      uint32_t pending = 0;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int i = i0 + u * PER;
-      pv[u] = i < (int)gridDim.x
-                  ? __hip_atomic_load(&part[(int64_t)i * B + bt],
-                                      __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT)
-                  : pack_partial(-INFINITY, INT_MAX);
-    }
+      for (int u = 0; u < UNR; ++u)
+        if (i0 + u * NT < nblk) pending |= 1u << u;
+      for (int spin = 0; pending != 0; ++spin) {
+        uint64_t tv[UNR], tr[UNR];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const float fv = __uint_as_float((uint32_t)pv[u]);
-      const int fr = (int)(pv[u] >> 32);
-      if (better(fv, fr, v, r)) {
-        v = fv;
-        r = fr;
+        for (int u = 0; u < UNR; ++u) {
+          tv[u] = tr[u] = 0;
+          if ((pending >> u) & 1u) {
+            const FinishSlot* s = slot + (int64_t)(i0 + u * NT) * B + b;
+            tv[u] = __hip_atomic_load(&s->tv, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            tr[u] = __hip_atomic_load(&s->tr, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          if (!((pending >> u) & 1u) || (tv[u] >> 32) != tg ||
+              (tr[u] >> 32) != tg)
+            continue;
+          pending &= ~(1u << u);
+          const float fv = __uint_as_float((uint32_t)tv[u]);
+          const int fr = (int)(uint32_t)tr[u];
+          if (better(fv, fr, v, r)) {
+            v = fv;
+            r = fr;
+            // fetched now, so the winner's id is usually in hand by the end
+            if (fr >= 0 && fr < a.n_rows) id = a.dh_idx[fr];
+          }
+        }
+        if (pending != 0) {
+          if (spin >= FINISH_SPIN_LIMIT) {
+            failed = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
       }
     }
-  }
-#pragma unroll
-  for (int off = B; off < 64; off <<= 1) {
-    const float ov = __shfl_xor(v, off, 64);
-    const int orow = __shfl_xor(r, off, 64);
-    if (better(ov, orow, v, r)) {
-      v = ov;
-      r = orow;
+    // Block argmax of (v, r); the thread holding the winning row (rows are
+    // unique within a column) writes its id, so no thread waits for another
+    // thread's dh_idx fetch.
+    float wvv = v;
+    int wr = r;
+    wave_argmax(wvv, wr);
+    if (lane == 0) {
+      cv[wave] = wvv;
+      cr[wave] = wr;
     }
-  }
-  if (lane < B) {
-    sv[wave][lane] = v;
-    sr[wave][lane] = r;
-  }
-  __syncthreads();
-  if (threadIdx.x < B && threadIdx.x < a.nb) {
-    const int b = threadIdx.x;
-    float fv = sv[0][b];
-    int fr = sr[0][b];
+    __syncthreads();
+    float fv = cv[0];
+    int fr = cr[0];
     for (int w = 1; w < NW; ++w)
-      if (better(sv[w][b], sr[w][b], fv, fr)) {
-        fv = sv[w][b];
-        fr = sr[w][b];
+      if (better(cv[w], cr[w], fv, fr)) {
+        fv = cv[w];
+        fr = cr[w];
       }
-    if (fr < 0 || fr >= a.n_rows) fr = 0;  // only reachable with NaN inputs
-    a.out_ids[b] = a.dh_idx[fr];
+    if (fr >= 0 && fr < a.n_rows) {
+      if (r == fr) a.out_ids[b] = failed ? -1 : id;
+    } else if (threadIdx.x == 0) {
+      // no row won: only reachable when every logit is NaN
+      a.out_ids[b] = failed ? -1 : a.dh_idx[0];
+    }
+    __syncthreads();  // cv/cr are reused by the next column
   }
+  // Block 0 collects column 0, so it has seen every block's slot, and with
+  // it every block's read of the counter, before it advances the counter.
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(a.ws + WS_EPOCH), tg,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every lane holds a candidate for each of the B columns: one wave argmax
+// per column.
+template <int B, int NT>
+__device__ __forceinline__ void argmax_finish(float (&best_v)[B],
+                                              int (&best_r)[B],
+                                              const KArgs& a,
+                                              uint32_t epoch) {
+  static_assert((B & (B - 1)) == 0, "batch slots are a power of two");
+  __shared__ WaveBest<B, NT> w;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    wave_argmax(best_v[b], best_r[b]);
+    if (lane == 0) {
+      w.v[wave][b] = best_v[b];
+      w.r[wave][b] = best_r[b];
+    }
+  }
+  finish_from_waves<B, NT>(w, a, epoch);
+}
+
+// MFMA output layout: the 16 lanes of row q = lane / 16 hold the candidates
+// of columns 4q + j in register j.  Four 16-lane DPP reductions, which run
+// on the four rows at once, replace sixteen whole-wave ones.
+template <int NT>
+__device__ __forceinline__ void argmax_finish_rows(float (&best_v)[4],
+                                                   int (&best_r)[4],
+                                                   const KArgs& a,
+                                                   uint32_t epoch) {
+  __shared__ WaveBest<16, NT> w;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    row_argmax(best_v[j], best_r[j]);
+    if ((lane & 15) == 0) {
+      w.v[wave][4 * (lane >> 4) + j] = best_v[j];
+      w.r[wave][4 * (lane >> 4) + j] = best_r[j];
+    }
+  }
+  finish_from_waves<16, NT>(w, a, epoch);
 }
 
 }  // namespace dh

@@ -17,6 +17,7 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
   constexpr int HD = F::EPU / 2;  // h dwords per unit
   extern __shared__ uint4 hs4[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t epoch = LOGITS ? 0u : finish_epoch(a);
   {
     const uint4* src = reinterpret_cast<const uint4*>(a.h);
     const int n = (int)(B * a.hidden / 8);
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
       }
     }
   }
-  if constexpr (!LOGITS) argmax_finish<B, THREADS>(best_v, best_r, a);
+  if constexpr (!LOGITS) argmax_finish<B, THREADS>(best_v, best_r, a, epoch);
 }
 
 template <class F, bool L>

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t epoch = LOGITS ? 0u : finish_epoch(a);
   const int64_t hidden = a.hidden;
   const int nb = a.nb;
 
@@ -297,15 +298,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   }
   if constexpr (!LOGITS) {
     // batch row b lives in register b%4 of the lanes with l/16 == b/4
-    float bv[16];
-    int br[16];
-#pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const bool own = q == (b >> 2);
-      bv[b] = own ? best_v[b & 3] : -INFINITY;
-      br[b] = own ? best_r[b & 3] : INT_MAX;
-    }
-    argmax_finish<16, NT>(bv, br, a);
+    argmax_finish_rows<NT>(best_v, best_r, a, epoch);
   }
 }
 
