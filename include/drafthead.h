@@ -38,9 +38,14 @@
  *    (page 1, load_draft_model pads the index so the NVFP4 GEMM row count is
  *    a multiple of 64).  draft_head_build_index produces it.
  *  - Workspace: device memory of at least draft_head_workspace_bytes() bytes,
- *    zero-filled once by the caller before its first use.  The kernels leave
- *    it zeroed again when they finish.  Calls that may run concurrently need
- *    distinct workspaces.
+ *    zero-filled once by the caller before its first use.  From then on it
+ *    carries state from call to call (a call counter and per-block results
+ *    tagged with it), so the caller must not modify it between calls; calls
+ *    may share it whatever their head or batch size, and replaying a
+ *    captured call is safe.  Calls that may run concurrently need distinct
+ *    workspaces.  A top-token call whose blocks could not all publish
+ *    within seconds (only possible if the device starves some of them)
+ *    writes -1 for the affected batch rows.
  *  - Every function returns DH_OK (0) or a negative DH_E* code; no C++
  *    exception crosses this interface.  Arguments are checked on the host
  *    before any device work is enqueued.  Ids outside [0, vocab) and

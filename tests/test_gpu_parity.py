@@ -207,6 +207,37 @@ def test_top_tokens_workspace_shared_across_heads_and_batches():
             assert torch.equal(shared.cpu(), fresh.cpu()), (k, b)
 
 
+@pytest.mark.parametrize("name,batch", [("flash_next_64k", 1), ("tiny", 16)])
+def test_top_tokens_graph_replay(name, batch):
+    """A captured top-token call replayed with new hidden states matches the
+    eager call every time: the call counter in the workspace advances on the
+    device, so replays never mistake the previous replay's slots for theirs."""
+    hd = head(name)
+    ws = dh.new_workspace(hd.n_rows, batch)
+    h_static = torch.zeros(batch, hd.hidden, dtype=torch.bfloat16, device=DEV)
+    out = torch.full((batch,), -7, dtype=torch.int32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up call outside the capture
+        dh.draft_head_top_tokens(hd.packed, hd.scales, hd.gs, hd.idx_gpu,
+                                 h_static, out_ids=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dh.draft_head_top_tokens(hd.packed, hd.scales, hd.gs, hd.idx_gpu,
+                                 h_static, out_ids=out, workspace=ws)
+    for k in range(5):
+        h = wl.hidden_states(batch, hd.hidden, 900 + k).to(DEV)
+        want = dh.draft_head_top_tokens(hd.packed, hd.scales, hd.gs,
+                                        hd.idx_gpu, h).cpu()
+        h_static.copy_(h)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), want), k
+
+
 def _synthetic_head(rng, n_rows, hidden):
     packed = rng.integers(0, 256, size=(n_rows, hidden // 2), dtype=np.uint8)
     scales = rng.integers(0x20, 0x48, size=(n_rows, hidden // 16), dtype=np.uint8)
