@@ -11,13 +11,15 @@
 //   1. k_gather_amax   max |x| over the gathered rows as an atomicMax on the
 //                      binary32 bit pattern (exact and order-independent for
 //                      non-negative floats);
-//   2. k_nvfp4_encode  one thread per 16-element block: block max, E4M3
-//                      scale, 16 e2m1 codes packed into 8 bytes;
+//   2. k_nvfp4_encode  two lanes per 16-element block: block max, E4M3
+//                      scale, 8 e2m1 codes per lane packed into 4 bytes;
 //   3. k_quant_finish  writes the global scale and returns the amax slot of
 //                      the workspace to zero.
-// Every float operation is a single IEEE binary32 operation with
-// round-to-nearest-even (no contraction, correctly rounded division), in the
-// order gs = max(amax,1e-12)/2688, s = bmax/(6*gs), q = x/(e4m3(s)*gs).
+// Every float result is the single IEEE binary32 operation the recipe names,
+// with round-to-nearest-even (no contraction), in the order
+// gs = max(amax,1e-12)/2688, s = bmax/(6*gs), q = x/(e4m3(s)*gs); the
+// per-element quotients are the correctly rounded divisions, computed with
+// Markstein's correction (below).
 //
 // Per-tensor E4M3 (page 2, "FP8 MTP draft stack for vLLM",
 // _fp8_convert_draft_head: one scale amax/448 for the whole head, elements
@@ -33,10 +35,19 @@ namespace dh {
 namespace {
 
 constexpr int QTHREADS = 256;
+constexpr int QWAVES = QTHREADS / 64;
 
 __device__ __forceinline__ uint32_t abs_bf16_pair_max(uint32_t v) {
   uint32_t lo = v & 0x7FFFu, hi = (v >> 16) & 0x7FFFu;
   return lo > hi ? lo : hi;
+}
+
+__device__ __forceinline__ uint32_t abs_bf16_max8(const uint4& v) {
+  uint32_t a = abs_bf16_pair_max(v.x), b = abs_bf16_pair_max(v.y);
+  uint32_t c = abs_bf16_pair_max(v.z), d = abs_bf16_pair_max(v.w);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
 }
 
 __device__ __forceinline__ float global_scale_from(uint32_t amax_bits) {
@@ -44,83 +55,225 @@ __device__ __forceinline__ float global_scale_from(uint32_t amax_bits) {
   return fmaxf(amax, 1e-12f) / 2688.0f;
 }
 
+// Correctly rounded quotients without a division per element.  Given
+// rd = RN(1/d) (one correctly rounded division per divisor),
+// q0 = RN(ax * rd) is within an ulp of ax / d, the residual
+// r = ax - q0 * d is exact in one fma, and RN(q0 + r * rd) is the correctly
+// rounded quotient (Markstein's correction).  The kernels use it for d in
+// [2^-60, 2^60] and ax <= 2^60 (no overflow; a subnormal ax then gives a
+// quotient below 2^-66, where every e2m1 and E4M3 decision is 0 whatever
+// the last bits) and divide otherwise.  Equality with the division over
+// every bf16 ax in that range was checked by brute force on the CPU.
+__device__ __forceinline__ bool divisor_in_range(float d) {
+  return d >= 0x1p-60f && d <= 0x1p60f;
+}
+
+// e2m1 magnitude index of RN-to-nearest-even of q >= 0 (or NaN -> 0),
+// saturating at 6.  Below 1 the two midpoints 0.25 and 0.75 are counted
+// (0.25 -> 0 and 0.75 -> 2 by ties-to-even); from 1 up the code is the
+// float's exponent and top mantissa bit after rounding the pattern at that
+// bit (a carry moves into the exponent).  Checked against counting all
+// seven midpoints for every non-negative float and NaN.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  const uint32_t lo = (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f);
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t t = u + 0x1FFFFFu + ((u >> 22) & 1u);
+  uint32_t c = (t >> 22) - 252u;  // 1.0 = exponent 127 -> code 2
+  c = c < 7u ? c : 7u;
+  return q >= 1.0f ? c : lo;
+}
+
+// The gathered rows in tiles of 64 16-byte units (512 elements) of one row:
+// a wave takes a tile, lane i its unit i, so the row and its source id are
+// wave-uniform and every load instruction reads 1 KB contiguous.
+struct Tiles {
+  int64_t per_row, count;
+  __device__ Tiles(int64_t hidden, int64_t n_rows)
+      : per_row((hidden / 8 + 63) / 64), count(n_rows * per_row) {}
+};
+
 __global__ __launch_bounds__(QTHREADS) void k_gather_amax(
     const uint16_t* __restrict__ w, int64_t hidden,
     const int32_t* __restrict__ ids, int64_t n_rows,
     uint32_t* __restrict__ amax_bits) {
-  const int64_t upr = hidden / 8;  // 16-byte units per row
-  const int64_t total = n_rows * upr;
+  const Tiles tl(hidden, n_rows);
+  const int lane = threadIdx.x & 63;
+  const int64_t upr = hidden / 8;
+  const int64_t wave = (int64_t)blockIdx.x * QWAVES +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * QWAVES;
   uint32_t m = 0;
-  for (int64_t u = (int64_t)blockIdx.x * QTHREADS + threadIdx.x; u < total;
-       u += (int64_t)gridDim.x * QTHREADS) {
-    int64_t j = u / upr, k = u - j * upr;
-    const uint4 v =
-        *reinterpret_cast<const uint4*>(w + (int64_t)ids[j] * hidden + k * 8);
-    uint32_t a = abs_bf16_pair_max(v.x), b = abs_bf16_pair_max(v.y);
-    uint32_t c = abs_bf16_pair_max(v.z), d = abs_bf16_pair_max(v.w);
-    a = a > b ? a : b;
-    c = c > d ? c : d;
-    a = a > c ? a : c;
-    m = m > a ? m : a;
+  // four tiles per round, all loads issued before any is used
+  for (int64_t t0 = wave; t0 < tl.count; t0 += 4 * nwaves) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t t = t0 + u * nwaves;
+      const int64_t j = t / tl.per_row;
+      const int64_t k = (t - j * tl.per_row) * 64 + lane;
+      v[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (t < tl.count && k < upr)
+        v[u] = *reinterpret_cast<const uint4*>(w + (int64_t)ids[j] * hidden +
+                                               k * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t a = abs_bf16_max8(v[u]);
+      m = m > a ? m : a;
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     uint32_t o = __shfl_xor(m, off, 64);
     m = m > o ? m : o;
   }
-  __shared__ uint32_t wmax[QTHREADS / 64];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __shared__ uint32_t wmax[QWAVES];
+  if (lane == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = wmax[0];
-    for (int i = 1; i < QTHREADS / 64; ++i) r = r > wmax[i] ? r : wmax[i];
+    for (int i = 1; i < QWAVES; ++i) r = r > wmax[i] ? r : wmax[i];
     // |bf16| bits shifted into place are the binary32 bits of the same
     // non-negative value, whose unsigned order is the numeric order.
     if (r) atomicMax(amax_bits, r << 16);
   }
 }
 
+// Tiles per round of the encoders: all loads of a round are issued before
+// any is used, so a wave keeps 4 KB in flight.
+constexpr int ROUND = 4;
+
+// Tile t of a round (last tiles first, see below): its row, first unit and
+// the load of this lane's 16 bytes (a lane past the row's end re-reads the
+// row's last block pair).  Tiles past the end repeat tile 0.
+struct TileLoad {
+  int64_t j, k;
+  bool live;
+  uint4 v;
+};
+
+__device__ __forceinline__ TileLoad load_tile(const uint16_t* w,
+                                              int64_t hidden,
+                                              const int32_t* ids,
+                                              const Tiles& tl, int64_t i,
+                                              int lane) {
+  TileLoad r;
+  const int64_t upr = hidden / 8;
+  const int64_t t = i < tl.count ? tl.count - 1 - i : 0;
+  r.j = t / tl.per_row;
+  const int64_t k0 = (t - r.j * tl.per_row) * 64;
+  r.live = i < tl.count && k0 + lane < upr;
+  r.k = k0 + lane < upr ? k0 + lane : upr - 2 + (lane & 1);
+  r.v = *reinterpret_cast<const uint4*>(w + (int64_t)ids[r.j] * hidden +
+                                        r.k * 8);
+  return r;
+}
+
+// Hardware converts with scale 1.0.  A hardware probe over every float bit
+// pattern found:
+//   * v_cvt_scalef32_pk_fp4_f32 rounds to the nearest e2m1 value, ties to
+//     even, saturates at 6 and keeps the sign (-0 gives 0x8): exactly the
+//     element code of the recipe applied to the quotient;
+//   * v_cvt_scalef32_pk_fp8_f32 rounds to the nearest E4M3 value, ties to
+//     even, up to 464, and gives the NaN code beyond: exact for inputs
+//     clamped to +-448.
+// src0 goes to the low nibble (fp4) or the low byte (fp8).
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t old, float a, float b,
+                                             int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 3);
+  }
+}
+
+typedef short short2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t fp8_pair(float a, float b) {
+  const short2_t z = {0, 0};
+  const short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a, b, 1.0f,
+                                                              false);
+  return (uint32_t)(uint16_t)r[0];
+}
+
+// The largest bf16 magnitude (bits) of the Markstein quotient's range.
+constexpr uint32_t BF16_2P60 = 0x5D80u;
+
+// One lane per 8 elements, two lanes (i, i^1) per 16-element block.  The
+// encode pass walks the tiles from the last to the first: the amax pass has
+// just read the same bytes in the opposite order, so the first tiles read
+// here are the ones most likely still in the device's last-level cache.
+// Per element the fast path is one Markstein quotient and half a hardware
+// convert; a wave that has a block outside the Markstein range (a NaN,
+// |x| > 2^60 or an extreme divisor) encodes the tile with the division and
+// the midpoint count instead.
 __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
     const uint16_t* __restrict__ w, int64_t hidden,
     const int32_t* __restrict__ ids, int64_t n_rows,
     const uint32_t* __restrict__ amax_bits, uint8_t* __restrict__ packed,
     uint8_t* __restrict__ scales) {
-  const int64_t nblk = hidden / 16;
-  const int64_t total = n_rows * nblk;
+  const Tiles tl(hidden, n_rows);
+  const int lane = threadIdx.x & 63;
   const float gs = global_scale_from(*amax_bits);
   const float six_gs = 6.0f * gs;
-  for (int64_t u = (int64_t)blockIdx.x * QTHREADS + threadIdx.x; u < total;
-       u += (int64_t)gridDim.x * QTHREADS) {
-    int64_t j = u / nblk, b = u - j * nblk;
-    const uint4* src = reinterpret_cast<const uint4*>(
-        w + (int64_t)ids[j] * hidden + b * 16);
-    const uint4 v0 = src[0], v1 = src[1];
-    uint32_t x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t bm = 0;
+  const int64_t wave = (int64_t)blockIdx.x * QWAVES +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * QWAVES;
+  for (int64_t i0 = wave; i0 < tl.count; i0 += ROUND * nwaves) {
+    TileLoad ld[ROUND];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t a = abs_bf16_pair_max(x[i]);
-      bm = bm > a ? bm : a;
-    }
-    const float bmax = bf16_to_f32(bm);
-    const float s = bmax / six_gs;
-    const uint32_t sc = e4m3_encode_nonneg(s);
-    const float s_dec = e4m3_decode_nonneg(sc);
-    const float d = s_dec * gs;
-    uint32_t out[2] = {0u, 0u};
+    for (int u = 0; u < ROUND; ++u)
+      ld[u] = load_tile(w, hidden, ids, tl, i0 + u * nwaves, lane);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t bits = (x[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      uint32_t nib = (bits >> 15) << 3;  // sign bit of the BF16 input
-      if (s_dec != 0.0f) {
-        const float q = bf16_to_f32(bits) / d;
-        nib |= e2m1_encode_mag(fabsf(q));
+    for (int u = 0; u < ROUND; ++u) {
+      const uint4 v = ld[u].v;
+      uint32_t bm = abs_bf16_max8(v);
+      const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(
+          0, (int)bm, DPP_QUAD_1032, 0xF, 0xF, false);
+      bm = bm > other ? bm : other;
+      const float bmax = bf16_to_f32(bm);
+      const float s = bmax / six_gs;
+      const uint32_t sc = e4m3_encode_nonneg(s);
+      const float s_dec = e4m3_decode_nonneg(sc);
+      const float d = s_dec * gs;
+      const bool zero = s_dec == 0.0f;
+      const float rd = 1.0f / d;
+      const bool fast = zero || (divisor_in_range(d) && bm <= BF16_2P60);
+      const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+      uint32_t out = 0;
+      if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float q[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t bits = (x[(e + h) >> 1] >> (((e + h) & 1) * 16)) &
+                                  0xFFFFu;
+            const float ax = bf16_to_f32(bits & 0x7FFFu);
+            const float q0 = ax * rd;
+            const float r = __builtin_fmaf(-q0, d, ax);
+            const float mag = zero ? 0.0f : __builtin_fmaf(r, rd, q0);
+            q[h] = __uint_as_float(__float_as_uint(mag) |
+                                   ((bits & 0x8000u) << 16));
+          }
+          out = fp4_pair(out, q[0], q[1], e >> 1);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+          const float ax = bf16_to_f32(bits & 0x7FFFu);
+          const uint32_t mag = zero ? 0u : e2m1_code(ax / d);
+          out |= (((bits >> 15) << 3) | mag) << (4 * e);
+        }
       }
-      out[i >> 3] |= nib << ((i & 7) * 4);
+      if (ld[u].live) {
+        const int64_t j = ld[u].j, k = ld[u].k;
+        // element 2i in the low nibble of byte i
+        *reinterpret_cast<uint32_t*>(packed + j * (hidden / 2) + k * 4) = out;
+        if ((lane & 1) == 0) scales[j * (hidden / 16) + k / 2] = (uint8_t)sc;
+      }
     }
-    *reinterpret_cast<uint2*>(packed + j * (hidden / 2) + b * 8) =
-        make_uint2(out[0], out[1]);
-    scales[j * nblk + b] = (uint8_t)sc;
   }
 }
 
@@ -129,31 +282,64 @@ __device__ __forceinline__ float e4m3_scale_from(uint32_t amax_bits) {
   return fmaxf(amax, 1e-12f) / 448.0f;
 }
 
+// One lane per 8 elements, tiles from the last to the first (as above).
+// Fast path: Markstein quotient, clamp, hardware convert; a wave with an
+// element outside the Markstein range takes the division and the software
+// encode instead.
 __global__ __launch_bounds__(QTHREADS) void k_e4m3_encode(
     const uint16_t* __restrict__ w, int64_t hidden,
     const int32_t* __restrict__ ids, int64_t n_rows,
     const uint32_t* __restrict__ amax_bits, uint8_t* __restrict__ q) {
-  const int64_t upr = hidden / 8;  // 16-byte input units per row
-  const int64_t total = n_rows * upr;
+  const Tiles tl(hidden, n_rows);
+  const int lane = threadIdx.x & 63;
   const float scale = e4m3_scale_from(*amax_bits);
-  for (int64_t u = (int64_t)blockIdx.x * QTHREADS + threadIdx.x; u < total;
-       u += (int64_t)gridDim.x * QTHREADS) {
-    const int64_t j = u / upr, k = u - j * upr;
-    const uint4 v =
-        *reinterpret_cast<const uint4*>(w + (int64_t)ids[j] * hidden + k * 8);
-    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
-    uint32_t out[2] = {0u, 0u};
+  const float rs = 1.0f / scale;
+  const bool scale_fast = divisor_in_range(scale);
+  const int64_t wave = (int64_t)blockIdx.x * QWAVES +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * QWAVES;
+  for (int64_t i0 = wave; i0 < tl.count; i0 += ROUND * nwaves) {
+    TileLoad ld[ROUND];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t bits = (x[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      float t = bf16_to_f32(bits) / scale;
-      t = fminf(fmaxf(t, -448.0f), 448.0f);
-      const uint32_t code =
-          e4m3_encode_nonneg(fabsf(t)) | ((__float_as_uint(t) >> 31) << 7);
-      out[i >> 2] |= code << ((i & 3) * 8);
+    for (int u = 0; u < ROUND; ++u)
+      ld[u] = load_tile(w, hidden, ids, tl, i0 + u * nwaves, lane);
+#pragma unroll
+    for (int u = 0; u < ROUND; ++u) {
+      const uint32_t x[4] = {ld[u].v.x, ld[u].v.y, ld[u].v.z, ld[u].v.w};
+      const bool fast = scale_fast && abs_bf16_max8(ld[u].v) <= BF16_2P60;
+      uint32_t out[2] = {0u, 0u};
+      if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float t[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t bits = (x[(e + h) >> 1] >> (((e + h) & 1) * 16)) &
+                                  0xFFFFu;
+            const float ax = bf16_to_f32(bits & 0x7FFFu);
+            const float q0 = ax * rs;
+            const float r = __builtin_fmaf(-q0, scale, ax);
+            const float mag = fminf(__builtin_fmaf(r, rs, q0), 448.0f);
+            t[h] = __uint_as_float(__float_as_uint(mag) |
+                                   ((bits & 0x8000u) << 16));
+          }
+          out[e >> 2] |= fp8_pair(t[0], t[1]) << ((e & 2) * 8);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+          float t = bf16_to_f32(bits) / scale;
+          t = fminf(fmaxf(t, -448.0f), 448.0f);
+          const uint32_t code =
+              e4m3_encode_nonneg(fabsf(t)) | ((__float_as_uint(t) >> 31) << 7);
+          out[e >> 2] |= code << ((e & 3) * 8);
+        }
+      }
+      if (ld[u].live)
+        *reinterpret_cast<uint2*>(q + ld[u].j * hidden + ld[u].k * 8) =
+            make_uint2(out[0], out[1]);
     }
-    *reinterpret_cast<uint2*>(q + j * hidden + k * 8) =
-        make_uint2(out[0], out[1]);
   }
 }
 
@@ -168,9 +354,12 @@ __global__ void k_quant_finish(uint32_t* __restrict__ amax_bits,
   }
 }
 
-int grid_for(int64_t units, int cus) {
-  int64_t want = (units + QTHREADS - 1) / QTHREADS;
-  int64_t cap = (int64_t)cus * 16;
+// Blocks for n_rows gathered rows: one wave per tile, at most 8 blocks of
+// 4 waves per CU (one resident round at the kernels' register use).
+int grid_for(int64_t n_rows, int64_t hidden, int cus) {
+  const int64_t tiles = n_rows * ((hidden / 8 + 63) / 64);
+  int64_t want = (tiles + QWAVES - 1) / QWAVES;
+  const int64_t cap = (int64_t)cus * 8;
   if (want > cap) want = cap;
   return (int)(want < 1 ? 1 : want);
 }
@@ -182,11 +371,11 @@ hipError_t launch_nvfp4_quantize(const QuantArgs& a, hipStream_t s) {
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
   uint32_t* amax = reinterpret_cast<uint32_t*>(a.ws + WS_AMAX);
-  k_gather_amax<<<grid_for(a.n_rows * (a.hidden / 8), di.cus), QTHREADS, 0,
-                  s>>>(a.w, a.hidden, a.ids, a.n_rows, amax);
-  k_nvfp4_encode<<<grid_for(a.n_rows * (a.hidden / 16), di.cus), QTHREADS, 0,
-                   s>>>(a.w, a.hidden, a.ids, a.n_rows, amax, a.packed,
-                        a.scales);
+  const int grid = grid_for(a.n_rows, a.hidden, di.cus);
+  k_gather_amax<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
+                                          amax);
+  k_nvfp4_encode<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
+                                           amax, a.packed, a.scales);
   k_quant_finish<false><<<1, 64, 0, s>>>(amax, a.global_scale);
   return hipGetLastError();
 }
@@ -196,7 +385,7 @@ hipError_t launch_e4m3_quantize(const QuantE4m3Args& a, hipStream_t s) {
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
   uint32_t* amax = reinterpret_cast<uint32_t*>(a.ws + WS_AMAX);
-  const int grid = grid_for(a.n_rows * (a.hidden / 8), di.cus);
+  const int grid = grid_for(a.n_rows, a.hidden, di.cus);
   k_gather_amax<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
                                           amax);
   k_e4m3_encode<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
