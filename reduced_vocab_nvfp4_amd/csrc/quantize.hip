@@ -60,10 +60,12 @@ __device__ __forceinline__ float global_scale_from(uint32_t amax_bits) {
 // q0 = RN(ax * rd) is within an ulp of ax / d, the residual
 // r = ax - q0 * d is exact in one fma, and RN(q0 + r * rd) is the correctly
 // rounded quotient (Markstein's correction).  The kernels use it for d in
-// [2^-60, 2^60] and ax <= 2^60 (no overflow; a subnormal ax then gives a
-// quotient below 2^-66, where every e2m1 and E4M3 decision is 0 whatever
-// the last bits) and divide otherwise.  Equality with the division over
-// every bf16 ax in that range was checked by brute force on the CPU.
+// [2^-60, 2^60] and ax <= 2^60 (no overflow) and divide otherwise.  Where
+// ax is below about 2^-100 the residual underflows and the result can be an
+// ulp off, but the quotient is then below 2^-40, and every e2m1 and E4M3
+// code of a quotient below 2^-11 is 0 whatever its last bits.  Equality
+// with the division for every quotient of at least 2^-24, over every bf16
+// ax in range, is checked by brute force on the CPU (tests/native).
 __device__ __forceinline__ bool divisor_in_range(float d) {
   return d >= 0x1p-60f && d <= 0x1p60f;
 }

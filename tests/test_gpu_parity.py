@@ -118,6 +118,59 @@ def test_quantize_edge_cases():
     assert np.array_equal(p.cpu().numpy(), packed) and g.item() == 2.0 ** -8
 
 
+def _sweep_head(rng, e_lo, e_hi):
+    """BF16 head whose blocks of 16 put every positive bf16 value x with a
+    biased exponent in [e_lo, e_hi) (subnormals too when e_lo == 0) beside a
+    block maximum x*f for twelve factors f, so that the quotient x/d of the
+    element code falls near every e2m1 midpoint; the other 13 elements are
+    x times seeded factors in [0, 1) with seeded signs."""
+    ex = np.arange(e_lo, e_hi, dtype=np.uint32)
+    x = ((ex[:, None] << 7) | np.arange(128, dtype=np.uint32)[None, :]).ravel()
+    x = x[x > 0]
+    xf = (x << 16).view(np.float32)
+    factors = np.array([1, 1.25, 1.5, 2, 2.5, 3, 4, 5, 6, 8, 12, 24],
+                       dtype=np.float32)
+    nb = x.size * factors.size
+    blk = np.empty((nb, 16), dtype=np.float32)
+    xs = np.repeat(xf, factors.size)
+    big = xs.astype(np.float64) * np.tile(factors, x.size)
+    # below the largest finite bf16, and never below x after rounding
+    blk[:, 0] = np.maximum(np.minimum(big, 3.38e38), xs).astype(np.float32)
+    blk[:, 1] = xs
+    blk[:, 2] = -xs
+    blk[:, 3:] = (xs[:, None] * rng.random((nb, 13), dtype=np.float32)
+                  * rng.choice(np.array([-1, 1], dtype=np.float32), (nb, 13)))
+    pad = -nb % 16  # whole rows of 256: repeat the first blocks
+    blk = np.concatenate([blk, blk[:pad]])
+    w = torch.from_numpy(blk.reshape(-1, 256)).to(torch.bfloat16)
+    # the block maximum stays the largest magnitude after rounding to bf16
+    a = w.float().abs().view(-1, 16)
+    assert bool((a[:, 0] >= a.max(dim=1).values).all())
+    return w
+
+
+def test_quantizers_on_every_finite_bf16_value():
+    """Both quantizers against the oracle, bit for bit, over every finite
+    bf16 magnitude: windows of eight binades (so every block scale lands in
+    the E4M3 range) cover the exponent field, each value beside twelve block
+    maxima.  Pins the kernels' quotient (one reciprocal per divisor plus a
+    correction) and their hardware fp4/fp8 converts, including the windows
+    above 2^60 that take the division."""
+    rng = np.random.default_rng(77)
+    for e_lo in range(0, 255, 8):
+        e_hi = min(e_lo + 8, 255)
+        w = _sweep_head(rng, e_lo, e_hi)
+        idx = np.arange(w.shape[0], dtype=np.int32)
+        say(f"[quantize sweep] exponents [{e_lo}, {e_hi}) rows={w.shape[0]}")
+        _quant_case(w, idx)
+        q, sc = dh.e4m3_quantize_rows_per_tensor(w.to(DEV),
+                                                 torch.from_numpy(idx).to(DEV))
+        oq, os_ = oracle.e4m3_tensor_quantize(wl.bf16_bits(w), idx)
+        assert np.float32(sc.item()) == os_
+        qn = q.cpu().numpy()
+        assert np.array_equal(qn, oq), (e_lo, np.argwhere(qn != oq)[:5])
+
+
 # ------------------------------------------------------------ top tokens
 
 def _top_tokens_check(hd, h, tag):

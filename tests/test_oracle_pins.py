@@ -6,6 +6,7 @@ fixture, or an invariant, chosen so that a dropped term, a wrong sign, a
 swapped nibble or index, a wrong constant or a wrong tie rule fails a test.
 None of these tests needs a GPU.
 """
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -375,3 +376,19 @@ def test_e4m3_tensor_reading_divides_by_the_scale():
     assert wb.float()[5, 3].item() == 1.1399388313293457e-06
     q, scale = oracle.e4m3_tensor_quantize(_bits(wb), np.arange(64, dtype=np.int32))
     assert q[5, 3] == 26 and q[0, 0] == 0x7E
+
+
+def test_markstein_quotient_equals_the_division(tmp_path):
+    """The quantizer kernels' per-element quotient (one reciprocal per
+    divisor, Markstein's fma correction) is the correctly rounded division
+    over every bf16 input in its range, for a seeded sample of divisors: the
+    arithmetic fact the kernels rely on, checked on the CPU's IEEE float32
+    with a correctly rounded fmaf."""
+    import subprocess
+    src = os.path.join(os.path.dirname(__file__), "native", "markstein_check.c")
+    exe = str(tmp_path / "markstein_check")
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", src,
+                    "-o", exe, "-lm"], check=True)
+    r = subprocess.run([exe, "1500"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout
+    assert "mismatches 0 " in r.stdout, r.stdout
