@@ -44,6 +44,16 @@ from reduced_vocab_nvfp4_amd import workloads as wl  # noqa: E402
 
 METRIC = ("draft-head µs/step and HBM GB/s (% peak), NVFP4 64064x2560 "
           "GEMV+argmax, batch 1")
+
+
+def metric_name(case) -> str:
+    """The headline metric for the default workload; the same measure named
+    for the workload otherwise."""
+    if case.name == "flash_next_64k" and case.op == "top":
+        return METRIC
+    what = "GEMV+argmax" if case.op == "top" else "GEMV+logits scatter"
+    return (f"draft-head µs/step and HBM GB/s (% peak), {case.fmt.upper()} "
+            f"{case.n_rows}x{case.H} {what}, batch {case.B}")
 HBM_PEAK_GBS = 8000.0
 INFINITY_CACHE = 256 << 20
 RTOL, ATOL = 1e-3, 1e-4
@@ -406,7 +416,7 @@ def main():
 
     khash = kernel_source_hash()
     rec = {
-        "metric": METRIC,
+        "metric": metric_name(case),
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
