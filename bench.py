@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -78,12 +79,22 @@ def algorithmic_bytes(fmt, n_rows, hidden, batch, op, vocab):
     return b
 
 
-def kernel_source_hash():
+def code_text(src: str) -> str:
+    """C/C++/HIP source without comments and with whitespace collapsed: what
+    the compiler sees, so a comment edit does not mark measurements stale.
+    (The kernel sources hold no "//" or "/*" inside string literals.)"""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def kernel_source_hash(csrc=None):
+    """Hash of the kernel sources' code (comments and layout excluded)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "reduced_vocab_nvfp4_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "reduced_vocab_nvfp4_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,8 +15,8 @@ static bool aligned(const void* p, uintptr_t n) {
 
 size_t workspace_bytes(int64_t n_rows, int64_t batch) {
   if (n_rows < 1 || batch < 1 || batch > MAX_BATCH) return 0;
-  // A batch of one runs the one-row kernels; any larger batch may run a
-  // kernel that keeps MAX_SLICE partials per block.
+  // A batch of one runs the one-row kernels (one argmax slot per block);
+  // any larger batch may run a kernel with MAX_SLICE slots per block.
   const int64_t slots = batch == 1 ? 1 : MAX_SLICE;
   return WS_SLOTS + (size_t)MAX_GRID * (size_t)slots * 16;
 }

@@ -83,10 +83,10 @@ __device__ __forceinline__ uint32_t finish_epoch(const KArgs& a) {
 }
 
 // Block-level (value,row) reduction, the partial write and the collection
-// of the partials.  best_v/best_r are this lane's candidates for the B batch columns of
-// the slice (B = the slice's compile-time capacity; only the first a.nb are
-// written out).  epoch = finish_epoch(a), loaded at the kernel's start (only
-// thread 0's value is used).
+// of the partials.  best_v/best_r are this lane's candidates for the B batch
+// columns of the slice (B = the slice's compile-time capacity; only the
+// first a.nb are written out).  epoch = finish_epoch(a), loaded at the
+// kernel's start (only thread 0's value is used).
 //
 // Cross-block protocol.  Every block publishes its (value, row) per batch
 // column in a slot of two 64-bit words, (tag, value bits) and (tag, row),
@@ -95,18 +95,18 @@ __device__ __forceinline__ uint32_t finish_epoch(const KArgs& a) {
 // its own share of the rows, polls the slots of column 0 with agent-scope
 // atomic loads until both words carry this call's tag; a slot can only hold
 // that tag once this call's owner wrote it, and the values travel inside
-// the atomics, so relaxed ordering suffices.  (Batch columns past the first
-// are collected the same way by blocks 1, 2, ...)  A collector learns of the last slot
-// about one memory round trip after it lands, where counting arrivals costs
-// a completion wait and an atomic round trip per counter level.  While it
+// the atomics, so relaxed ordering suffices.  Column b is collected the same
+// way by block b % gridDim.x.  A collector learns of the last slot about one
+// memory round trip after it lands, where counting arrivals costs a
+// completion wait and an atomic round trip per counter level.  While it
 // polls, a collector also fetches dh_idx of each running best row, so the
 // winner's id is usually in hand when the last slot arrives.
 //
-// The wait is bounded: after FINISH_SPIN_LIMIT empty polls (seconds) a
-// collector gives up and writes -1 for its batch row.  No block waits on a
-// block that is not running: the collectors only wait for slots, and every
-// other block publishes without waiting, so the grid drains whatever the
-// dispatch order.
+// Termination: only the collectors (at most 16 blocks) wait, and only for
+// slots that the other blocks publish without waiting on anything, so those
+// blocks run to completion wherever and whenever they are dispatched and
+// every wait ends.  The wait is also bounded: after FINISH_SPIN_LIMIT empty
+// polls (seconds) a collector gives up and writes -1 for its batch row.
 constexpr int FINISH_SPIN_LIMIT = 1 << 22;
 
 struct FinishSlot {
