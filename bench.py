@@ -276,9 +276,33 @@ def cpu_baseline(case, h_list, budget_s):
         i += 1
         if time.perf_counter() - t_start > budget_s or i >= 64:
             break
-    return {"step_s": float(np.median(times)), "steps": len(times),
-            "threads": oracle.num_threads(), "quantize_s": t_quant,
+    threads = oracle.num_threads()
+    step_s = float(np.median(times))
+    # one step on one thread, when it fits the budget (about threads x the
+    # parallel step)
+    single_s = None
+    if step_s * threads <= budget_s:
+        oracle.set_threads(1)
+        try:
+            t0 = time.perf_counter()
+            case.oracle_step(h_list[0])
+            single_s = time.perf_counter() - t0
+        finally:
+            oracle.set_threads(threads)
+    return {"step_s": step_s, "steps": len(times), "threads": threads,
+            "single_thread_s": single_s, "quantize_s": t_quant,
             "results": results}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def check_top(ids, results, case, n_h):
@@ -419,10 +443,13 @@ def main():
             "us_per_step": round(cb["step_s"] * 1e6, 1),
             "cores": cb["threads"],
             "kind": "oracle",
+            "single_thread_us_per_step": (
+                round(cb["single_thread_s"] * 1e6, 1)
+                if cb["single_thread_s"] is not None else None),
             "sample": (f"{cb['steps']} full steps of {case.name} (float64 "
                        f"GEMV over {case.n_rows} rows x {H}, batch {B}, "
                        f"{what}), median; host {os.cpu_count()} visible "
-                       f"CPUs"),
+                       f"CPUs, {cpu_model()}"),
         }
 
     khash = kernel_source_hash()

@@ -91,12 +91,12 @@ __device__ __forceinline__ uint32_t finish_epoch(const KArgs& a) {
 // Cross-block protocol.  Every block publishes its (value, row) per batch
 // column in a slot of two 64-bit words, (tag, value bits) and (tag, row),
 // each written by an agent-scope atomic store (single-copy atomic, performed
-// past the per-XCD L2), and exits without waiting for them.  Block 0, after
-// its own share of the rows, polls the slots of column 0 with agent-scope
-// atomic loads until both words carry this call's tag; a slot can only hold
-// that tag once this call's owner wrote it, and the values travel inside
-// the atomics, so relaxed ordering suffices.  Column b is collected the same
-// way by block b % gridDim.x.  A collector learns of the last slot about one
+// past the per-XCD L2), and exits without waiting for them.  The last block,
+// after its own share of the rows, polls the slots of column 0 with
+// agent-scope atomic loads until both words carry this call's tag; a slot
+// can only hold that tag once this call's owner wrote it, and the values
+// travel inside the atomics, so relaxed ordering suffices.  Column b is
+// collected the same way by block gridDim.x - 1 - b % gridDim.x.  A collector learns of the last slot about one
 // memory round trip after it lands, where counting arrivals costs a
 // completion wait and an atomic round trip per counter level.  While it
 // polls, a collector also fetches dh_idx of each running best row, so the
@@ -159,14 +159,16 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
   // Collection.  Batch column b < min(nb, B) is collected by block
-  // b % gridDim.x, so the columns of a wide slice are polled from different
-  // CUs (the uncached polling loads of one CU are served one after another).
+  // gridDim.x - 1 - b % gridDim.x: the columns of a wide slice are polled
+  // from different CUs (the uncached polling loads of one CU are served one
+  // after another), and the collectors are the blocks dispatched last,
+  // which tend to finish last, so most slots are there by their first poll.
   // Thread t polls the slots of blocks t + k * NT, UNR of them per round,
   // and re-reads only those still pending.
   const int nblk = (int)gridDim.x;
   const int ncol = a.nb < B ? a.nb : B;
   constexpr int UNR = 8;
-  for (int b = blockIdx.x; b < ncol; b += nblk) {
+  for (int b = nblk - 1 - (int)blockIdx.x; b < ncol; b += nblk) {
     float v = -INFINITY;
     int r = INT_MAX;
     int id = 0;  // dh_idx[r] once r is a row
@@ -238,9 +240,10 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
     }
     __syncthreads();  // cv/cr are reused by the next column
   }
-  // Block 0 collects column 0, so it has seen every block's slot, and with
-  // it every block's read of the counter, before it advances the counter.
-  if (blockIdx.x == 0 && threadIdx.x == 0)
+  // The last block collects column 0, so it has seen every block's slot, and
+  // with it every block's read of the counter, before it advances the
+  // counter.
+  if ((int)blockIdx.x == nblk - 1 && threadIdx.x == 0)
     __hip_atomic_store(reinterpret_cast<uint32_t*>(a.ws + WS_EPOCH), tg,
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
