@@ -15,6 +15,8 @@ Workloads (reduced_vocab_nvfp4_amd/workloads.py; seeded synthetic inputs):
   dense27b_64k_b8  NVFP4 64 064 x 5120, batch 8, fp32 logits to 248 320 ids
   stock_bf16       BF16 248 320 x 2560 (every id), batch 1, top token
   tiny             NVFP4 1024 x 256, batch 1 (launch-bound; correctness)
+  linear_*         NVFP4 W4A16 linears of the drafter's block (nvfp4_linear,
+                   dense fp32 out; no index, no argmax)
 
 The timed region streams from HBM: R copies of the head rotate so that
 R x head bytes exceeds twice the 256 MB Infinity Cache.  Timing: HIP events
@@ -52,6 +54,9 @@ def metric_name(case) -> str:
     for the workload otherwise."""
     if case.name == "flash_next_64k" and case.op == "top":
         return METRIC
+    if case.op == "linear":
+        return (f"NVFP4 W4A16 linear µs/step and HBM GB/s (% peak), "
+                f"{case.n_rows}x{case.H}, batch {case.B}")
     what = "GEMV+argmax" if case.op == "top" else "GEMV+logits scatter"
     return (f"draft-head µs/step and HBM GB/s (% peak), {case.fmt.upper()} "
             f"{case.n_rows}x{case.H} {what}, batch {case.B}")
@@ -74,6 +79,8 @@ def algorithmic_bytes(fmt, n_rows, hidden, batch, op, vocab):
     b += 4 if fmt != "bf16" else 0
     if op == "logits":
         b += n_rows * 4 + batch * vocab * 4
+    elif op == "linear":
+        b += batch * n_rows * 4
     else:
         b += batch * 4 + batch * 4
     return b
@@ -123,7 +130,11 @@ class Case:
             raise SystemExit(f"workload {config} has no {fmt} head "
                              f"(formats: {', '.join(w_.formats)})")
         self.V, self.H, self.B = w_.vocab, w_.hidden, w_.batch
-        default_op = "logits" if w_.logits and w_.batch > 1 else "top"
+        default_op = ("linear" if w_.linear else
+                      "logits" if w_.logits and w_.batch > 1 else "top")
+        if w_.linear and op not in (None, "linear"):
+            raise SystemExit(f"workload {config} is a linear; --op does not "
+                             f"apply")
         self.op = op or default_op
         self.name = config if fmt == w_.formats[0] else f"{config}_{fmt}"
         if self.op != default_op:
@@ -187,6 +198,16 @@ class Case:
         n, H, B, R, nh = self.n_rows, self.H, self.B, self.R, len(h_ptrs)
         out_p = out.data_ptr()
         fmt = self.fmt
+        if self.op == "linear":
+            stride = B * n * 4
+
+            def step(i):
+                hd = heads[i % R]
+                rc = L.nvfp4_linear(hd[0], hd[1], sc, n, H, h_ptrs[i % nh], B,
+                                    out_p + stride * (i % 2), sp)
+                if rc:
+                    raise dh.DraftHeadError("linear", rc)
+            return step
         if self.op == "logits":
             stride = B * self.V * 4
             nk, V = self.n_kept, self.V
@@ -254,6 +275,8 @@ class Case:
             L = oracle.bf16_logits(self.o_head, self.idx, hb)
         if self.op == "logits":
             return L, oracle.logits_scatter(L, self.n_kept, self.idx, self.V)
+        if self.op == "linear":
+            return L, L
         return L, oracle.argmax_remap(L, self.idx)[1]
 
 
@@ -347,8 +370,9 @@ def main():
                     choices=["nvfp4", "e4m3", "bf16"],
                     help="head format (default: the workload's first)")
     ap.add_argument("--op", default=None, choices=["top", "logits"],
-                    help="step kind (default: logits for the batch-8 "
-                         "logits workload, else top tokens)")
+                    help="step kind of a head workload (default: logits for "
+                         "the batch-8 logits workload, else top tokens); "
+                         "the linear workloads always run the linear")
     ap.add_argument("--rotate", type=int, default=0,
                     help="head copies to rotate (0: enough for 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -386,8 +410,9 @@ def main():
     elif case.head_bytes >= 2 * INFINITY_CACHE:
         R = 1
     else:
-        # small heads are launch-bound: a few copies are enough
-        R = min(16, -(-2 * INFINITY_CACHE // case.head_bytes) + 1)
+        # enough copies that every step reads its weights from HBM, as a
+        # decode step does when the model's weights exceed the cache
+        R = min(4096, -(-2 * INFINITY_CACHE // case.head_bytes) + 1)
     case.rotate(R)
     n_h = 8
     h_cpu = [wl.hidden_states(B, H, s) for s in range(n_h)]
@@ -396,6 +421,9 @@ def main():
     K, W = args.steps, args.warmup
     if case.op == "logits":
         out = torch.empty((2, B, V), dtype=torch.float32, device=dev)
+    elif case.op == "linear":
+        out = torch.empty((2, B, case.n_rows), dtype=torch.float32,
+                          device=dev)
     else:
         out = torch.zeros((K + W, B), dtype=torch.int32, device=dev)
     step = case.make_step(h_ptrs, out, stream)
@@ -427,7 +455,7 @@ def main():
     result_cpu, parity = None, None
     if not args.no_cpu_baseline:
         cb = cpu_baseline(case, h_cpu, args.cpu_budget)
-        if case.op == "logits":
+        if case.op in ("logits", "linear"):
             # the last timed step used h[(K-1) % n_h] and buffer (K-1) % 2
             hi = (K - 1) % n_h
             ref = (cb["results"][hi] if hi < len(cb["results"])
@@ -436,7 +464,8 @@ def main():
         else:
             parity = check_top(out[:K].cpu().numpy(), cb["results"], case,
                                n_h)
-        what = "logits scatter" if case.op == "logits" else "argmax, remap"
+        what = {"logits": "logits scatter", "linear": "dense fp32 out",
+                "top": "argmax, remap"}[case.op]
         result_cpu = {
             "value": round(case.nbytes / cb["step_s"] / 1e9, 3),
             "unit": "GB/s",
@@ -472,8 +501,9 @@ def main():
             "n_rows": case.n_rows, "n_kept": case.n_kept,
             "format": {"nvfp4": "nvfp4-w4a16", "e4m3": "e4m3-w8a16",
                        "bf16": "bf16"}[fmt],
-            "step": ("top tokens" if case.op == "top" else
-                     "fp32 logits to the full vocab"),
+            "step": {"top": "top tokens",
+                     "logits": "fp32 logits to the full vocab",
+                     "linear": "NVFP4 W4A16 linear, fp32 out"}[case.op],
             "rotated_head_copies": R, "parallelism": "none (1 GPU)",
         },
         "roofline": {

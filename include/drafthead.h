@@ -154,6 +154,25 @@ int draft_head_logits(const uint8_t* packed, const uint8_t* scales,
                       size_t workspace_bytes, void* stream);
 
 /*
+ * NVFP4 W4A16 linear for the drafter's other projections (page 1,
+ * "q38_draft.py", install: every 2-D BF16 weight of the MTP block named in
+ * its key list, with N % 64 == 0 and K % 16 == 0, is quantized with the same
+ * recipe and its forward returns the quantized linear's output).  Quantize
+ * the weight with nvfp4_quantize_rows and an identity row_ids.
+ *   packed, scales, global_scale [device] the NVFP4 weight, n_rows x hidden
+ *   h_bf16  [device] batch x hidden BF16 inputs
+ *   out     [device] out: batch x n_rows float32, row-major
+ * out[b, j] = global_scale * sum_k e2m1*e4m3*h[b,k], accumulated in float32
+ * (never rounded to BF16).  No workspace: nothing crosses blocks.
+ * Errors: DH_EINVAL for null or misaligned pointers (out 16 bytes), hidden %
+ * 16 != 0, hidden < 16, hidden > 16384, n_rows < 64 or n_rows % 64 != 0,
+ * batch < 1 or batch > 64; DH_EHIP.
+ */
+int nvfp4_linear(const uint8_t* packed, const uint8_t* scales,
+                 const float* global_scale, int64_t n_rows, int64_t hidden,
+                 const void* h_bf16, int64_t batch, float* out, void* stream);
+
+/*
  * Per-tensor E4M3 head from the same gathered rows (page 2, "FP8 MTP draft
  * stack for vLLM", _fp8_convert_draft_head: the FP8 head it ships scales the whole head by amax/448, divides, clamps to
  * +-448 and casts to e4m3fn; page 3 lists the FP8 head next to the NVFP4 one).

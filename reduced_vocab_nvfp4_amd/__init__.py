@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
                                         _c_i64, _c_i64, _c_i64, _c_i64,
                                         _c_ptr, _c_i64, _c_ptr, _c_ptr,
                                         _c_size, _c_ptr]
+        L.nvfp4_linear.restype = ctypes.c_int
+        L.nvfp4_linear.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64,
+                                   _c_ptr, _c_i64, _c_ptr, _c_ptr]
         L.e4m3_quantize_rows_per_tensor.restype = ctypes.c_int
         L.e4m3_quantize_rows_per_tensor.argtypes = [
             _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr,
@@ -228,6 +231,25 @@ def draft_head_logits(packed, scales, global_scale, dh_idx, n_kept: int,
     return out
 
 
+# ---------------------------------------------- NVFP4 W4A16 linear (N1)
+
+def nvfp4_linear(packed, scales, global_scale, h, *, out=None, stream=None):
+    """float32 [B, n_rows] = global_scale * (NVFP4 weight) @ h^T, for a
+    weight quantized by nvfp4_quantize_rows (identity row_ids)."""
+    n, H2 = packed.shape
+    B, H = h.shape
+    dev = h.device
+    if out is None:
+        out = torch.empty((B, n), dtype=torch.float32, device=dev)
+    rc = lib().nvfp4_linear(
+        _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
+        _dev(global_scale, "global_scale", torch.float32), n, H,
+        _dev(h, "h", torch.bfloat16), B, _dev(out, "out", torch.float32),
+        _stream(dev, stream))
+    _check("nvfp4_linear", rc)
+    return out
+
+
 # ------------------------------------------- per-tensor E4M3 head (FP8)
 
 def e4m3_quantize_rows_per_tensor(w: torch.Tensor, row_ids: torch.Tensor, *,
@@ -339,7 +361,7 @@ def draft_head_logits_bf16(w, dh_idx, n_kept: int, vocab: int, h, *,
 __all__ = [
     "DraftHeadError", "lib", "error_string", "draft_head_build_index",
     "draft_head_workspace_bytes", "new_workspace", "nvfp4_quantize_rows",
-    "draft_head_top_tokens", "draft_head_logits",
+    "draft_head_top_tokens", "draft_head_logits", "nvfp4_linear",
     "e4m3_quantize_rows_per_tensor", "draft_head_top_tokens_e4m3",
     "draft_head_logits_e4m3", "draft_head_top_tokens_bf16",
     "draft_head_logits_bf16",

@@ -241,6 +241,33 @@ int draft_head_logits(const uint8_t* packed, const uint8_t* scales,
                     workspace, workspace_bytes, stream);
 }
 
+int nvfp4_linear(const uint8_t* packed, const uint8_t* scales,
+                 const float* global_scale, int64_t n_rows, int64_t hidden,
+                 const void* h_bf16, int64_t batch, float* out,
+                 void* stream) {
+  using namespace dh;
+  if (!packed || !scales || !global_scale || !h_bf16 || !out)
+    return DH_EINVAL;
+  if (!aligned(packed, 16) || !aligned(scales, 16) ||
+      !aligned(global_scale, 4) || !aligned(h_bf16, 16) || !aligned(out, 16))
+    return DH_EINVAL;
+  if (hidden < 16 || hidden > 16384 || hidden % 16 != 0) return DH_EINVAL;
+  if (n_rows < 64 || n_rows % 64 != 0 || n_rows > INT32_MAX) return DH_EINVAL;
+  if (batch < 1 || batch > MAX_BATCH) return DH_EINVAL;
+  GemvArgs a{};
+  a.fmt = FMT_NVFP4;
+  a.w = packed;
+  a.scales = scales;
+  a.scale = global_scale;
+  a.n_rows = n_rows;
+  a.hidden = hidden;
+  a.h = static_cast<const uint16_t*>(h_bf16);
+  a.batch = batch;
+  a.out_logits = out;
+  a.dense = true;
+  return status(launch_gemv(a, static_cast<hipStream_t>(stream)));
+}
+
 int draft_head_top_tokens_e4m3(const uint8_t* q, const float* scale,
                                const int32_t* dh_idx, int64_t n_rows,
                                int64_t hidden, const void* h_bf16,

@@ -68,6 +68,9 @@ struct GemvArgs {
   float* out_logits;  // logits mode when non-null
   int64_t n_kept, vocab;
   uint8_t* ws;
+  // Dense output (the linear): out_logits[b][j] for every row j, no index,
+  // no -inf fill; dh_idx, n_kept and vocab are ignored.
+  bool dense = false;
 };
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
 

@@ -66,7 +66,7 @@ __device__ __forceinline__ void load_rows(Rows<F, C>& r, const KArgs& a,
   }
 }
 
-template <class F, int G, int C, bool LOGITS>
+template <class F, int G, int C, int MODE>
 __device__ __forceinline__ void compute_rows(const Rows<F, C>& r,
                                              const KArgs& a, int64_t row,
                                              int g, const uint32_t* hreg,
@@ -78,8 +78,9 @@ __device__ __forceinline__ void compute_rows(const Rows<F, C>& r,
   for (int i = 0; i < C; ++i)
     acc = F::chunk_dot(r.p[i], F::SCALED ? r.s[i] : 0u, hreg + i * HD, acc);
   const float v = group_sum<G>(acc);
-  if constexpr (LOGITS) {
-    if (g == 0 && row < a.n_kept) a.out_logits[a.dh_idx[row]] = v * sc;
+  if constexpr (MODE != OUT_TOP) {
+    if (g == 0 && row < a.n_kept)
+      a.out_logits[out_col<MODE>(a.dh_idx, row)] = v * sc;
   } else if (v > best_v) {
     // rows reach a lane in ascending order: strict > keeps the lowest
     best_v = v;
@@ -89,8 +90,9 @@ __device__ __forceinline__ void compute_rows(const Rows<F, C>& r,
 
 // Format F, G lanes per row, C chunks per lane, NB register buffers, NT
 // threads per block.
-template <class F, int G, int C, bool LOGITS, int NB, int NT>
+template <class F, int G, int C, int MODE, int NB, int NT>
 __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
+  constexpr bool LOGITS = MODE != OUT_TOP;
   constexpr int R = 64 / G;  // rows per wave iteration
   constexpr int NW = NT / 64;
   constexpr int HD = F::EPC / 2;           // h dwords per chunk
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
                            lane_chunk);
         __builtin_amdgcn_sched_barrier(0);
         if (it + k < n_it)  // wave-uniform: padded iterations only load
-          compute_rows<F, G, C, LOGITS>(buf[k], a, row0_of(it + k) + grp, g,
+          compute_rows<F, G, C, MODE>(buf[k], a, row0_of(it + k) + grp, g,
                                         hreg, sc,
                                         best_v, best_r);
         __builtin_amdgcn_sched_barrier(0);
@@ -217,7 +219,7 @@ constexpr bool fits() {
          64 * 1024;
 }
 
-template <class F, int G, int C, bool L>
+template <class F, int G, int C, int L>
 bool desc(KernelDesc* d) {
   if constexpr (fits<F, G, C>()) {
     *d = KernelDesc{reinterpret_cast<const void*>(
@@ -229,7 +231,7 @@ bool desc(KernelDesc* d) {
 }
 
 // (G, C) for a row of n chunks: G*C == n, G a power of two <= 64, C <= 5.
-template <class F, bool L>
+template <class F, int L>
 bool pick(int64_t chunks, KernelDesc* d) {
   switch (chunks) {
     case 8: return desc<F, 8, 1, L>(d);
@@ -246,19 +248,26 @@ bool pick(int64_t chunks, KernelDesc* d) {
 }
 
 template <class F>
-bool pick_fmt(int64_t hidden, bool logits, KernelDesc* d) {
+bool pick_fmt(int64_t hidden, int mode, KernelDesc* d) {
   if (hidden % F::EPC != 0) return false;
   const int64_t chunks = hidden / F::EPC;
-  return logits ? pick<F, true>(chunks, d) : pick<F, false>(chunks, d);
+  switch (mode) {
+    case OUT_TOP: return pick<F, OUT_TOP>(chunks, d);
+    case OUT_SCATTER: return pick<F, OUT_SCATTER>(chunks, d);
+    case OUT_DENSE:
+      if constexpr (F::kFmt == FMT_NVFP4) return pick<F, OUT_DENSE>(chunks, d);
+      return false;
+  }
+  return false;
 }
 
 }  // namespace
 
-bool b1_kernel(int fmt, int64_t hidden, bool logits, KernelDesc* out) {
+bool b1_kernel(int fmt, int64_t hidden, int mode, KernelDesc* out) {
   switch (fmt) {
-    case FMT_NVFP4: return pick_fmt<Nvfp4>(hidden, logits, out);
-    case FMT_E4M3: return pick_fmt<E4m3>(hidden, logits, out);
-    case FMT_BF16: return pick_fmt<Bf16>(hidden, logits, out);
+    case FMT_NVFP4: return pick_fmt<Nvfp4>(hidden, mode, out);
+    case FMT_E4M3: return pick_fmt<E4m3>(hidden, mode, out);
+    case FMT_BF16: return pick_fmt<Bf16>(hidden, mode, out);
   }
   return false;
 }

@@ -20,6 +20,20 @@
 
 namespace dh {
 
+// What a GEMV launch writes: the top token per batch row (through the
+// argmax finish), the fp32 logits scattered to the full vocabulary at
+// dh_idx[j] for j < n_kept, or the fp32 output of every row densely,
+// out[b][j] (the plain linear).
+enum OutMode : int { OUT_TOP = 0, OUT_SCATTER = 1, OUT_DENSE = 2 };
+
+// Output column of row j in the logits modes.
+template <int MODE>
+__device__ __forceinline__ int64_t out_col(const int32_t* dh_idx,
+                                           int64_t row) {
+  if constexpr (MODE == OUT_DENSE) return row;
+  return dh_idx[row];
+}
+
 // One launch = one batch slice of at most 16 rows.
 struct KArgs {
   const uint8_t* w;       // weight rows (format-specific bytes)
@@ -31,7 +45,7 @@ struct KArgs {
   int nb;             // batch rows in this slice
   int32_t* out_ids;   // [nb], top-token mode
   float* out_logits;  // [nb][vocab], logits mode
-  int64_t n_kept, vocab;
+  int64_t n_kept, vocab;  // dense mode: n_kept = n_rows, vocab = row stride
   uint8_t* ws;
 };
 
@@ -45,10 +59,11 @@ struct KernelDesc {
 };
 
 // Kernel families; each returns false when it has no kernel for the shape.
-bool b1_kernel(int fmt, int64_t hidden, bool logits, KernelDesc* out);
-bool mfma_kernel(int fmt, int64_t hidden, int nb, bool logits,
+// mode is an OutMode; the dense mode exists for NVFP4 only.
+bool b1_kernel(int fmt, int64_t hidden, int mode, KernelDesc* out);
+bool mfma_kernel(int fmt, int64_t hidden, int nb, int mode,
                  int lds_per_block, KernelDesc* out);
-bool generic_kernel(int fmt, int nb, int64_t hidden, bool logits,
+bool generic_kernel(int fmt, int nb, int64_t hidden, int mode,
                     KernelDesc* out);
 // Largest batch slice the MFMA kernel can stage for this hidden size.
 int mfma_max_slice(int64_t hidden, int lds_per_block);

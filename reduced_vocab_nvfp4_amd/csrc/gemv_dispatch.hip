@@ -34,10 +34,15 @@ int generic_slice(int64_t remaining, int64_t hidden) {
   return 1;
 }
 
+int out_mode(const GemvArgs& ga) {
+  if (ga.out_logits == nullptr) return OUT_TOP;
+  return ga.dense ? OUT_DENSE : OUT_SCATTER;
+}
+
 hipError_t plan_slice(const GemvArgs& ga, int64_t remaining,
                       const DeviceInfo& di, KernelDesc* d, int* bc) {
-  const bool logits = ga.out_logits != nullptr;
-  if (remaining == 1 && b1_kernel(ga.fmt, ga.hidden, logits, d)) {
+  const int mode = out_mode(ga);
+  if (remaining == 1 && b1_kernel(ga.fmt, ga.hidden, mode, d)) {
     *bc = 1;
     return hipSuccess;
   }
@@ -45,13 +50,13 @@ hipError_t plan_slice(const GemvArgs& ga, int64_t remaining,
     int nb = mfma_max_slice(ga.hidden, di.lds_per_block);
     if (nb > remaining) nb = (int)remaining;
     if (nb >= 2 &&
-        mfma_kernel(ga.fmt, ga.hidden, nb, logits, di.lds_per_block, d)) {
+        mfma_kernel(ga.fmt, ga.hidden, nb, mode, di.lds_per_block, d)) {
       *bc = nb;
       return hipSuccess;
     }
   }
   *bc = generic_slice(remaining, ga.hidden);
-  return generic_kernel(ga.fmt, *bc, ga.hidden, logits, d)
+  return generic_kernel(ga.fmt, *bc, ga.hidden, mode, d)
              ? hipSuccess
              : hipErrorInvalidValue;
 }
@@ -63,7 +68,7 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
   const bool logits = ga.out_logits != nullptr;
-  if (logits) {
+  if (logits && !ga.dense) {
     const int64_t n = ga.batch * ga.vocab;
     int64_t blocks = (n / 4 + FILL_THREADS - 1) / FILL_THREADS;
     if (blocks > (int64_t)di.cus * 8) blocks = (int64_t)di.cus * 8;
@@ -96,15 +101,17 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     k.w = ga.w;
     k.scales = ga.scales;
     k.scale = ga.scale;
-    k.dh_idx = ga.dh_idx;
+    k.dh_idx = ga.dense ? nullptr : ga.dh_idx;
     k.n_rows = ga.n_rows;
     k.hidden = ga.hidden;
     k.h = ga.h + b0 * ga.hidden;
     k.nb = bc;
     k.out_ids = logits ? nullptr : ga.out_ids + b0;
-    k.out_logits = logits ? ga.out_logits + b0 * ga.vocab : nullptr;
-    k.n_kept = ga.n_kept;
-    k.vocab = ga.vocab;
+    // dense: every row is written, out has n_rows columns
+    const int64_t cols = ga.dense ? ga.n_rows : ga.vocab;
+    k.out_logits = logits ? ga.out_logits + b0 * cols : nullptr;
+    k.n_kept = ga.dense ? ga.n_rows : ga.n_kept;
+    k.vocab = cols;
     k.ws = ga.ws;
     void* kargs[] = {&k};
     e = hipLaunchKernel(d.fn, dim3((unsigned)grid), dim3(d.threads), kargs,

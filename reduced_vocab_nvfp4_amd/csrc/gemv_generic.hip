@@ -11,8 +11,9 @@ namespace {
 
 constexpr int THREADS = 256;
 
-template <class F, int B, bool LOGITS>
+template <class F, int B, int MODE>
 __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
+  constexpr bool LOGITS = MODE != OUT_TOP;
   constexpr int NW = THREADS / 64;
   constexpr int HD = F::EPU / 2;  // h dwords per unit
   extern __shared__ uint4 hs4[];
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
       const float v = group_sum<64>(acc[b]);
       if constexpr (LOGITS) {
         if (lane == 0 && row < a.n_kept)
-          a.out_logits[b * a.vocab + a.dh_idx[row]] = v * sc;
+          a.out_logits[b * a.vocab + out_col<MODE>(a.dh_idx, row)] = v * sc;
       } else if (v > best_v[b]) {
         best_v[b] = v;
         best_r[b] = (int)row;
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
   if constexpr (!LOGITS) argmax_finish<B, THREADS>(best_v, best_r, a, epoch);
 }
 
-template <class F, bool L>
+template <class F, int L>
 bool pick(int nb, KernelDesc* d) {
   const void* fn = nullptr;
   switch (nb) {
@@ -79,21 +80,29 @@ bool pick(int nb, KernelDesc* d) {
 }
 
 template <class F>
-bool pick_fmt(int nb, int64_t hidden, bool logits, KernelDesc* d) {
+bool pick_fmt(int nb, int64_t hidden, int mode, KernelDesc* d) {
   if (hidden % F::EPU != 0) return false;
-  if (!(logits ? pick<F, true>(nb, d) : pick<F, false>(nb, d))) return false;
+  bool ok = false;
+  switch (mode) {
+    case OUT_TOP: ok = pick<F, OUT_TOP>(nb, d); break;
+    case OUT_SCATTER: ok = pick<F, OUT_SCATTER>(nb, d); break;
+    case OUT_DENSE:
+      if constexpr (F::kFmt == FMT_NVFP4) ok = pick<F, OUT_DENSE>(nb, d);
+      break;
+  }
+  if (!ok) return false;
   d->lds_bytes = (size_t)nb * (size_t)hidden * 2;
   return true;
 }
 
 }  // namespace
 
-bool generic_kernel(int fmt, int nb, int64_t hidden, bool logits,
+bool generic_kernel(int fmt, int nb, int64_t hidden, int mode,
                     KernelDesc* out) {
   switch (fmt) {
-    case FMT_NVFP4: return pick_fmt<Nvfp4>(nb, hidden, logits, out);
-    case FMT_E4M3: return pick_fmt<E4m3>(nb, hidden, logits, out);
-    case FMT_BF16: return pick_fmt<Bf16>(nb, hidden, logits, out);
+    case FMT_NVFP4: return pick_fmt<Nvfp4>(nb, hidden, mode, out);
+    case FMT_E4M3: return pick_fmt<E4m3>(nb, hidden, mode, out);
+    case FMT_BF16: return pick_fmt<Bf16>(nb, hidden, mode, out);
   }
   return false;
 }

@@ -100,8 +100,9 @@ __device__ __forceinline__ void slot_steps(const Slot<F, RT, SPS>& b, int q,
   }
 }
 
-template <class F, int RT, int SPS, int NB, bool LOGITS, int NT>
+template <class F, int RT, int SPS, int NB, int MODE, int NT>
 __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
+  constexpr bool LOGITS = MODE != OUT_TOP;
   constexpr int NW = NT / 64;
   constexpr int UR = 16 * RT;  // rows per unit
   extern __shared__ uint4 hs[];
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
                 *reinterpret_cast<const uint16_t*>(sb + soff[t] + 8 * c);
           }
     }
-    if constexpr (LOGITS) {
+    if constexpr (MODE == OUT_SCATTER) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) b.ids[t] = a.dh_idx[row0 + 16 * t + n];
     }
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   constexpr int SCALE_LOADS =
       wide_scales<F, SPS>() ? SPS / 2 : (F::SCALED ? SPS : 0);
   constexpr int WEIGHT_LOADS =
-      (NB - 1) * (RT * (SPS + SCALE_LOADS) + (LOGITS ? RT : 0));
+      (NB - 1) * (RT * (SPS + SCALE_LOADS) + (MODE == OUT_SCATTER ? RT : 0));
   static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(WEIGHT_LOADS)
@@ -278,7 +279,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
               if constexpr (LOGITS) {
                 const int m = 4 * q + j;
                 if (m < nb && row < a.n_kept)
-                  a.out_logits[(int64_t)m * a.vocab + b.ids[t]] = v * sc;
+                  a.out_logits[(int64_t)m * a.vocab +
+                               (MODE == OUT_DENSE ? row : b.ids[t])] = v * sc;
               } else if (v > best_v[j]) {
                 // a lane's rows ascend: strict > keeps the lowest
                 best_v[j] = v;
@@ -325,7 +327,7 @@ struct MfmaShape<Nvfp4> {
   static constexpr int SPS = 4;
 };
 
-template <class F, int SPS, bool L>
+template <class F, int SPS, int L>
 KernelDesc desc() {
   constexpr int NT = MfmaShape<F>::THREADS;
   return KernelDesc{
@@ -335,7 +337,7 @@ KernelDesc desc() {
 
 // Steps per slot: the format's preferred size if it divides the steps of a
 // unit (hidden / (4 * EPC)), else the largest of 10, 4, 2, 1 that does.
-template <class F, bool L>
+template <class F, int L>
 KernelDesc desc_for(int64_t steps) {
   constexpr int P = MfmaShape<F>::SPS;
   if (steps % P == 0) return desc<F, P, L>();
@@ -345,8 +347,20 @@ KernelDesc desc_for(int64_t steps) {
   return desc<F, 1, L>();
 }
 
+// The dense output mode (the linear) exists for NVFP4 only.
+template <class F, int SPS>
+KernelDesc desc_dense() {
+  if constexpr (F::kFmt == FMT_NVFP4) return desc<F, SPS, OUT_DENSE>();
+  return KernelDesc{nullptr, 0, 0, 0, false};
+}
 template <class F>
-bool pick(int64_t hidden, int nb, bool logits, int lds_per_block,
+KernelDesc desc_dense_for(int64_t steps) {
+  if constexpr (F::kFmt == FMT_NVFP4) return desc_for<F, OUT_DENSE>(steps);
+  return KernelDesc{nullptr, 0, 0, 0, false};
+}
+
+template <class F>
+bool pick(int64_t hidden, int nb, int mode, int lds_per_block,
           KernelDesc* d) {
   if (hidden % (4 * F::EPC) != 0) return false;
   if (nb < 1 || nb > mfma_max_slice(hidden, lds_per_block)) return false;
@@ -354,9 +368,13 @@ bool pick(int64_t hidden, int nb, bool logits, int lds_per_block,
   // 16-byte scale pieces need 16-byte aligned scale rows; otherwise one step
   // per slot (the odd slot size loads the scales as 16-bit values)
   if (F::SCALED && (hidden / 16) % 16 != 0)
-    *d = logits ? desc<F, 1, true>() : desc<F, 1, false>();
+    *d = mode == OUT_TOP       ? desc<F, 1, OUT_TOP>()
+         : mode == OUT_SCATTER ? desc<F, 1, OUT_SCATTER>()
+                               : desc_dense<F, 1>();
   else
-    *d = logits ? desc_for<F, true>(steps) : desc_for<F, false>(steps);
+    *d = mode == OUT_TOP       ? desc_for<F, OUT_TOP>(steps)
+         : mode == OUT_SCATTER ? desc_for<F, OUT_SCATTER>(steps)
+                               : desc_dense_for<F>(steps);
   d->lds_bytes = (size_t)(nb + 1) * (size_t)mfma_lds_row_bytes(hidden);
   return true;
 }
@@ -370,12 +388,16 @@ int mfma_max_slice(int64_t hidden, int lds_per_block) {
   return nb < 0 ? 0 : (int)nb;
 }
 
-bool mfma_kernel(int fmt, int64_t hidden, int nb, bool logits,
+bool mfma_kernel(int fmt, int64_t hidden, int nb, int mode,
                  int lds_per_block, KernelDesc* out) {
   switch (fmt) {
-    case FMT_NVFP4: return pick<Nvfp4>(hidden, nb, logits, lds_per_block, out);
-    case FMT_E4M3: return pick<E4m3>(hidden, nb, logits, lds_per_block, out);
-    case FMT_BF16: return pick<Bf16>(hidden, nb, logits, lds_per_block, out);
+    case FMT_NVFP4: return pick<Nvfp4>(hidden, nb, mode, lds_per_block, out);
+    case FMT_E4M3:
+      return mode != OUT_DENSE &&
+             pick<E4m3>(hidden, nb, mode, lds_per_block, out);
+    case FMT_BF16:
+      return mode != OUT_DENSE &&
+             pick<Bf16>(hidden, nb, mode, lds_per_block, out);
   }
   return false;
 }

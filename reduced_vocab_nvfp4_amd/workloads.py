@@ -43,6 +43,7 @@ class Workload:
     logits: bool = False   # the step also scatters fp32 logits to the full vocab
     identity: bool = False  # stock head: every id kept, no mask
     tiny_choice: bool = False  # keep = forced tail + a random choice (small case)
+    linear: bool = False   # a plain NVFP4 linear: vocab = output rows, dense out
     note: str = field(default="", compare=False)
 
 
@@ -66,6 +67,22 @@ WORKLOADS = {
         forced_tail=256, logits=True,
         note="V=248320 H=5120, 64064 rows, NVFP4, B=8, top tokens and "
              "fp32 logits scattered to the full vocab"),
+    # The drafter's other NVFP4 linears (page 1, "q38_draft.py", install:
+    # the MTP block's 2-D weights with N % 64 == 0 and K % 16 == 0): shapes
+    # at the draft head's hidden size, output rows x input features.
+    "linear_2560x5120_b1": Workload(
+        "linear_2560x5120_b1", vocab=2560, hidden=5120, batch=1, n_keep=2560,
+        forced_tail=0, identity=True, linear=True,
+        note="NVFP4 W4A16 linear, 2560 outputs from 5120 inputs (two "
+             "2560-wide vectors concatenated), B=1, dense fp32 out"),
+    "linear_10240x2560_b1": Workload(
+        "linear_10240x2560_b1", vocab=10240, hidden=2560, batch=1,
+        n_keep=10240, forced_tail=0, identity=True, linear=True,
+        note="NVFP4 W4A16 linear, 10240 outputs from 2560 inputs, B=1"),
+    "linear_5120x2560_b16": Workload(
+        "linear_5120x2560_b16", vocab=5120, hidden=2560, batch=16,
+        n_keep=5120, forced_tail=0, identity=True, linear=True,
+        note="NVFP4 W4A16 linear, 5120 outputs from 2560 inputs, B=16 (MFMA)"),
     "h98k_b16": Workload(
         "h98k_b16", vocab=248320, hidden=2560, batch=16, n_keep=98304,
         forced_tail=256, formats=("nvfp4", "e4m3"),

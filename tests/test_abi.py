@@ -194,3 +194,27 @@ def test_e4m3_and_bf16_heads_reject_bad_arguments_on_the_host():
         assert f(n_kept=129) == dh.DH_EINVAL
         assert f(vocab=50) == dh.DH_EINVAL
         assert f(out=FAKE + 4) == dh.DH_EINVAL
+
+
+def test_linear_rejects_bad_arguments_on_the_host():
+    L = dh.lib()
+    base = dict(p=FAKE, s=FAKE, g=FAKE, n=128, H=256, h=FAKE, B=1, out=FAKE)
+
+    def lin(**kw):
+        a = {**base, **kw}
+        return L.nvfp4_linear(a["p"], a["s"], a["g"], a["n"], a["H"], a["h"],
+                              a["B"], a["out"], None)
+    assert lin(p=None) == dh.DH_EINVAL
+    assert lin(s=None) == dh.DH_EINVAL
+    assert lin(g=None) == dh.DH_EINVAL
+    assert lin(h=None) == dh.DH_EINVAL
+    assert lin(out=None) == dh.DH_EINVAL
+    assert lin(n=100) == dh.DH_EINVAL        # not a multiple of 64
+    assert lin(n=0) == dh.DH_EINVAL
+    assert lin(H=40) == dh.DH_EINVAL         # not a multiple of 16
+    assert lin(H=16400) == dh.DH_EINVAL
+    assert lin(B=0) == dh.DH_EINVAL
+    assert lin(B=65) == dh.DH_EINVAL
+    assert lin(p=FAKE + 8) == dh.DH_EINVAL   # 16-byte alignment
+    assert lin(out=FAKE + 4) == dh.DH_EINVAL
+    assert lin(g=FAKE + 2) == dh.DH_EINVAL
