@@ -47,6 +47,7 @@ struct KArgs {
   float* out_logits;  // [nb][vocab], logits mode
   int64_t n_kept, vocab;  // dense mode: n_kept = n_rows, vocab = row stride
   uint8_t* ws;
+  int ks_log2;  // MFMA dense mode: log2 of the waves that share a unit
 };
 
 // Kernel descriptor used by the dispatcher.
@@ -56,6 +57,8 @@ struct KernelDesc {
   int rows_per_unit;  // rows one wave owns per work unit
   size_t lds_bytes;   // dynamic LDS
   bool spread;        // units dealt wave-major: one block per unit suffices
+  int split_slots;    // > 0: the waves of a block may split a unit's
+                      // split_slots slots over the hidden dimension
 };
 
 // Kernel families; each returns false when it has no kernel for the shape.

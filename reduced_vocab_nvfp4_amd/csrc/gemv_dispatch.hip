@@ -95,6 +95,19 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     int64_t grid = (int64_t)di.cus * occ;
     const int64_t by_work = d.spread ? units : (units + waves - 1) / waves;
     if (grid > by_work) grid = by_work;
+    // Fewer units than twice the resident blocks leave most waves idle and
+    // each busy one a long chain of dependent slots: then 2^kl waves of a
+    // block share a unit over the hidden dimension, as many as keep every
+    // group to one unit and every wave to at least one slot.  The grid stays
+    // one block per CU, so the decode spreads over every CU.  (With more
+    // units the split's closing barrier costs more than it saves.)
+    int kl = 0;
+    if (d.split_slots > 0 && units < 2 * (int64_t)di.cus * occ) {
+      const int64_t resident = (int64_t)di.cus * occ * waves;
+      while ((2 << kl) <= waves && (2 << kl) <= d.split_slots &&
+             units * (2 << kl) <= resident)
+        ++kl;
+    }
     if (grid > MAX_GRID) grid = MAX_GRID;
     if (grid < 1) grid = 1;
     KArgs k;
@@ -113,6 +126,7 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     k.n_kept = ga.dense ? ga.n_rows : ga.n_kept;
     k.vocab = cols;
     k.ws = ga.ws;
+    k.ks_log2 = kl;
     void* kargs[] = {&k};
     e = hipLaunchKernel(d.fn, dim3((unsigned)grid), dim3(d.threads), kargs,
                         d.lds_bytes, s);

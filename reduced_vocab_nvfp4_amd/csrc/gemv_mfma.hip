@@ -18,7 +18,10 @@
 // h at the matching k from LDS.  A chunk holds EPC/8 MFMA operands.
 //
 // Work: a wave owns units of RT row tiles (16 rows each) and walks the whole
-// hidden dimension for each unit, one chunk per lane per tile per step.  A
+// hidden dimension for each unit, one chunk per lane per tile per step.  (In
+// the dense mode a small matrix has fewer units than the grid has waves:
+// then ks = 2^ks_log2 waves of a block share a unit, each walks a contiguous
+// part of its slots, and the block adds the parts through LDS, part 0 first.)  A
 // ring of NB register slots of SPS steps each keeps NB-1 slots of loads in
 // flight; the SPS loads of a tile are issued back to back so that DRAM sees
 // SPS*64 contiguous bytes of each row at once.  h of the
@@ -120,15 +123,22 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   const int PPR = (RBH + 1023) / 1024;
   const int SB = mfma_lds_row_bytes(hidden);
 
-  // Units are dealt wave-major (unit u goes to wave u / gridDim.x of block
-  // u % gridDim.x), so every block gets work even when there are fewer units
-  // than waves in the grid.
+  // Units are dealt to groups of ks waves, group-major (unit u goes to group
+  // u / gridDim.x of block u % gridDim.x), so every block gets work even when
+  // there are fewer units than groups in the grid.  Wave kp of a group takes
+  // slots [js0, js1) of each of its units; with ks > 1 the host guarantees
+  // at most one unit per group.
+  const int kl = MODE == OUT_DENSE ? a.ks_log2 : 0;
+  const int ks = 1 << kl;
+  const int gw = wv >> kl, kp = wv & (ks - 1);
   const int64_t U = a.n_rows / UR;
-  const int64_t TW = (int64_t)gridDim.x * NW;
-  const int64_t first = (int64_t)wv * gridDim.x + blockIdx.x;
+  const int64_t TW = (int64_t)gridDim.x * (NW >> kl);
+  const int64_t first = (int64_t)gw * gridDim.x + blockIdx.x;
   const int n_u = first < U ? (int)((U - first + TW - 1) / TW) : 0;
-  const int64_t CPR = hidden / F::EPC;    // 16-byte chunks per row
-  const int NS = (int)(CPR / (4 * SPS));  // slots per unit
+  const int64_t CPR = hidden / F::EPC;     // 16-byte chunks per row
+  const int NSU = (int)(CPR / (4 * SPS));  // slots per unit
+  const int js0 = (kp * NSU) >> kl, js1 = ((kp + 1) * NSU) >> kl;
+  const int NS = js1 - js0;                // slots of this wave per unit
   const int n_s = n_u * NS;
   const int n_pad = (n_s + NB - 1) / NB * NB;
   const int64_t RB = CPR * 16;      // weight bytes per row
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
 
   // Scalar cursor over (unit, slot) pairs: first row of the unit, slot.
   int64_t ld_row0 = (n_u > 0 ? first : 0) * UR;
-  int ld_js = 0, ld_count = 0;
+  int ld_js = js0, ld_count = 0;
   const int64_t unit_stride = TW * UR;
   auto load = [&](Slot<F, RT, SPS>& b) {
     // The cursor is passed through an opaque asm so that the compiler never
@@ -188,8 +198,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
     // padded ring re-read it (L2 hits) and are never computed.
     if (ld_count + 1 < n_s) {
       ++ld_count;
-      if (++ld_js == NS) {
-        ld_js = 0;
+      if (++ld_js == js1) {
+        ld_js = js0;
         ld_row0 += unit_stride;
       }
     }
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   int64_t cp_row0 = (n_u > 0 ? first : 0) * UR;
-  int cp_js = 0;
+  int cp_js = js0;
   for (int s0 = 0; s0 < n_pad; s0 += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
@@ -268,10 +278,11 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
         const Slot<F, RT, SPS>& b = buf[k];
         slot_steps<F, 0, RT, SPS>(
             b, q, hsb + hoff + cp_js * SPS * (4 * F::EPC * 2), acc);
-        if (cp_js == NS - 1) {
-          // unit done: rows row0 + 16t + n, batch rows 4q + j
+        if (cp_js == js1 - 1) {
+          // unit done: rows row0 + 16t + n, batch rows 4q + j (a split
+          // unit's parts are added after the loop)
 #pragma unroll
-          for (int t = 0; t < RT; ++t) {
+          for (int t = 0; t < RT && ks == 1; ++t) {
             const int64_t row = cp_row0 + 16 * t + n;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -289,13 +300,40 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
             }
             acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           }
-          cp_js = 0;
+          cp_js = js0;
           cp_row0 += unit_stride;
         } else {
           ++cp_js;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if constexpr (MODE == OUT_DENSE) {
+    if (ks > 1) {  // block-uniform
+      // Every wave is done with h: its LDS takes the partial tiles.
+      __syncthreads();
+      f32x4* red = reinterpret_cast<f32x4*>(hs);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) red[(wv * RT + t) * 64 + lane] = acc[t];
+      __syncthreads();
+      if (kp == 0 && n_u > 0) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          f32x4 v = acc[t];
+          for (int p = 1; p < ks; ++p) {
+            const f32x4 o = red[((wv + p) * RT + t) * 64 + lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] += o[j];
+          }
+          const int64_t row = first * UR + 16 * t + n;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int m = 4 * q + j;
+            if (m < nb) a.out_logits[(int64_t)m * a.vocab + row] = v[j] * sc;
+          }
+        }
+      }
     }
   }
   if constexpr (!LOGITS) {
@@ -327,30 +365,31 @@ struct MfmaShape<Nvfp4> {
   static constexpr int SPS = 4;
 };
 
+// steps = hidden / (4 * EPC), the MFMA steps of a unit.
 template <class F, int SPS, int L>
-KernelDesc desc() {
+KernelDesc desc(int64_t steps) {
   constexpr int NT = MfmaShape<F>::THREADS;
   return KernelDesc{
       reinterpret_cast<const void*>(k_mfma<F, MFMA_RT, SPS, MFMA_NB, L, NT>),
-      NT, 16 * MFMA_RT, 0, true};
+      NT, 16 * MFMA_RT, 0, true, L == OUT_DENSE ? (int)(steps / SPS) : 0};
 }
 
 // Steps per slot: the format's preferred size if it divides the steps of a
-// unit (hidden / (4 * EPC)), else the largest of 10, 4, 2, 1 that does.
+// unit, else the largest of 10, 4, 2, 1 that does.
 template <class F, int L>
 KernelDesc desc_for(int64_t steps) {
   constexpr int P = MfmaShape<F>::SPS;
-  if (steps % P == 0) return desc<F, P, L>();
-  if (steps % 10 == 0) return desc<F, 10, L>();
-  if (steps % 4 == 0) return desc<F, 4, L>();
-  if (steps % 2 == 0) return desc<F, 2, L>();
-  return desc<F, 1, L>();
+  if (steps % P == 0) return desc<F, P, L>(steps);
+  if (steps % 10 == 0) return desc<F, 10, L>(steps);
+  if (steps % 4 == 0) return desc<F, 4, L>(steps);
+  if (steps % 2 == 0) return desc<F, 2, L>(steps);
+  return desc<F, 1, L>(steps);
 }
 
 // The dense output mode (the linear) exists for NVFP4 only.
 template <class F, int SPS>
-KernelDesc desc_dense() {
-  if constexpr (F::kFmt == FMT_NVFP4) return desc<F, SPS, OUT_DENSE>();
+KernelDesc desc_dense(int64_t steps) {
+  if constexpr (F::kFmt == FMT_NVFP4) return desc<F, SPS, OUT_DENSE>(steps);
   return KernelDesc{nullptr, 0, 0, 0, false};
 }
 template <class F>
@@ -368,14 +407,20 @@ bool pick(int64_t hidden, int nb, int mode, int lds_per_block,
   // 16-byte scale pieces need 16-byte aligned scale rows; otherwise one step
   // per slot (the odd slot size loads the scales as 16-bit values)
   if (F::SCALED && (hidden / 16) % 16 != 0)
-    *d = mode == OUT_TOP       ? desc<F, 1, OUT_TOP>()
-         : mode == OUT_SCATTER ? desc<F, 1, OUT_SCATTER>()
-                               : desc_dense<F, 1>();
+    *d = mode == OUT_TOP       ? desc<F, 1, OUT_TOP>(steps)
+         : mode == OUT_SCATTER ? desc<F, 1, OUT_SCATTER>(steps)
+                               : desc_dense<F, 1>(steps);
   else
     *d = mode == OUT_TOP       ? desc_for<F, OUT_TOP>(steps)
          : mode == OUT_SCATTER ? desc_for<F, OUT_SCATTER>(steps)
                                : desc_dense_for<F>(steps);
   d->lds_bytes = (size_t)(nb + 1) * (size_t)mfma_lds_row_bytes(hidden);
+  if (mode == OUT_DENSE) {
+    // a split unit's parts are added through LDS: one f32x4 per lane and
+    // tile of every wave
+    const size_t red = (size_t)d->threads * MFMA_RT * 16;
+    if (d->lds_bytes < red) d->lds_bytes = red;
+  }
   return true;
 }
 

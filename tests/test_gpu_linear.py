@@ -25,10 +25,17 @@ def say(*a):
 # (n_rows, hidden, batch): the drafter's fc projection (2 x 2560 -> 2560)
 # and expanding / contracting projections at its hidden sizes, at batch 1
 # (one-row kernel), 4 and 16 (MFMA) and 33 (two slices); a hidden size
-# that only the generic kernel tiles; the smallest shape.
+# that only the generic kernel tiles; the smallest shape.  On the MFMA
+# kernel the waves of a block split a unit's hidden dimension when the
+# matrix has few 16-row units: 2560 x 5120 splits 8 ways over 10 slots,
+# 5120 x 2560 4 ways over 5 slots (uneven parts), 1024 rows 4 ways;
+# 24 000 and 40 960 rows do not split; hidden 2688 takes one-step slots (21
+# per unit, split 16 ways); hidden 256 has one slot per unit and cannot
+# split.
 SHAPES = [(2560, 5120, 1), (10240, 2560, 1), (2560, 10240, 1),
           (5120, 2560, 4), (2560, 5120, 16), (1024, 2560, 33),
-          (128, 272, 3), (64, 16, 1)]
+          (24000, 2560, 2), (40960, 2560, 16), (640, 2688, 8),
+          (64, 256, 2), (128, 272, 3), (64, 16, 1)]
 
 
 @pytest.mark.parametrize("n,hid,batch", SHAPES)
