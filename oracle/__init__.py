@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
                                                   c_i64, c_ptr, c_ptr]
         L.oracle_e4m3_tensor_logits.argtypes = [c_ptr, ctypes.c_float, c_i64,
                                                 c_i64, c_ptr, c_i64, c_ptr]
+        L.oracle_fp8_tokens_quantize.argtypes = [c_ptr, c_i64, c_i64, c_ptr,
+                                                 c_ptr]
+        L.oracle_w8a8_logits.argtypes = [c_ptr, ctypes.c_float, c_i64, c_i64,
+                                         c_ptr, c_ptr, c_i64, c_ptr]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -218,6 +222,33 @@ def e4m3_tensor_logits(q: np.ndarray, scale, h_bits: np.ndarray) -> np.ndarray:
     _check(lib().oracle_e4m3_tensor_logits(_p(q), float(scale), n, H,
                                            _p(h_bits), B, _p(L)),
            "e4m3_tensor_logits")
+    return L
+
+
+def fp8_tokens_quantize(h_bits: np.ndarray):
+    """C10: (qx u8[B,H], sx float32[B]), one E4M3 scale per row of h."""
+    h_bits = np.ascontiguousarray(np.atleast_2d(h_bits), dtype=np.uint16)
+    B, H = h_bits.shape
+    qx = np.empty((B, H), dtype=np.uint8)
+    sx = np.empty(B, dtype=np.float32)
+    _check(lib().oracle_fp8_tokens_quantize(_p(h_bits), B, H, _p(qx), _p(sx)),
+           "fp8_tokens_quantize")
+    return qx, sx
+
+
+def w8a8_logits(q: np.ndarray, sw, qx: np.ndarray,
+                sx: np.ndarray) -> np.ndarray:
+    """C11: float64 [B, n] logits of an E4M3 head against E4M3 tokens."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    qx = np.ascontiguousarray(np.atleast_2d(qx), dtype=np.uint8)
+    sx = np.ascontiguousarray(sx, dtype=np.float32)
+    n, H = q.shape
+    B = qx.shape[0]
+    if qx.shape[1] != H or sx.shape != (B,):
+        raise ValueError("w8a8_logits: shapes do not agree")
+    L = np.empty((B, n), dtype=np.float64)
+    _check(lib().oracle_w8a8_logits(_p(q), float(sw), n, H, _p(qx), _p(sx),
+                                    B, _p(L)), "w8a8_logits")
     return L
 
 

@@ -27,6 +27,13 @@
  *   C9  E4M3 per-tensor head: scale = max(amax,1e-12)/448, clamp, E4M3 cast
  *                                                      -- page 2,
  *       _fp8_convert_draft_head; page 3, "How it was built" (98K head)
+ *   C10 per-token dynamic E4M3 activations: each row of h gets its own
+ *       scale max(amax_row, 1e-12)/448, then the same clamp and cast as C9
+ *                                                      -- page 2,
+ *       _Fp8DraftHeadMethod.apply (per-token dynamic activation quant)
+ *   C11 W8A8 logits: both operands E4M3, scaled by the token's and the
+ *       head's scale, accumulated in float64              -- page 2,
+ *       _Fp8DraftHeadMethod.apply (the scaled GEMM)
  *
  * Floating point: every float operation below is one IEEE binary32 operation
  * rounded to nearest-even (built with -ffp-contract=off, no fast-math, SSE).
@@ -343,6 +350,57 @@ int oracle_e4m3_tensor_logits(const uint8_t* q, float scale, int64_t n_rows,
                 acc += oracle_e4m3_value(q[j * hidden + k]) *
                        (double)bf16_value(h[b * hidden + k]);
             L[b * n_rows + j] = (double)scale * acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------- C10 per-token E4M3 activations */
+
+/* For every row b of h: sx[b] = max(amax_b, 1e-12) / 448 with amax_b the
+ * largest |h[b,k]|; each element is h / sx[b], clamped to [-448, 448] and
+ * cast to E4M3 (RNE, sign kept) -- the head's recipe of C9, one scale per
+ * token instead of one per tensor. */
+int oracle_fp8_tokens_quantize(const uint16_t* h, int64_t batch,
+                               int64_t hidden, uint8_t* qx, float* sx) {
+    if (hidden <= 0 || batch <= 0) return ORACLE_EINVAL;
+    init_grids();
+    for (int64_t b = 0; b < batch; ++b) {
+        const uint16_t* row = h + b * hidden;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < hidden; ++k) {
+            float a = fabsf(bf16_value(row[k]));
+            if (a > amax) amax = a;
+        }
+        float scale = fmaxf(amax, 1e-12f) / 448.0f;
+        sx[b] = scale;
+        for (int64_t k = 0; k < hidden; ++k) {
+            float v = bf16_value(row[k]) / scale;
+            if (v > 448.0f) v = 448.0f;
+            if (v < -448.0f) v = -448.0f;
+            uint8_t mag = oracle_e4m3_code(fabsf(v));
+            qx[b * hidden + k] = (uint8_t)((signbit(v) ? 0x80 : 0) | mag);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------ C11 W8A8 logits */
+
+/* L[b*n_rows + j] = sx[b] * sw * sum_k e4m3(q[j,k]) * e4m3(qx[b,k]) in
+ * float64 (each product of two E4M3 values is exact). */
+int oracle_w8a8_logits(const uint8_t* q, float sw, int64_t n_rows,
+                       int64_t hidden, const uint8_t* qx, const float* sx,
+                       int64_t batch, double* L) {
+    if (hidden <= 0 || n_rows <= 0 || batch <= 0) return ORACLE_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t j = 0; j < n_rows; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < hidden; ++k)
+                acc += oracle_e4m3_value(q[j * hidden + k]) *
+                       oracle_e4m3_value(qx[b * hidden + k]);
+            L[b * n_rows + j] = (double)sx[b] * (double)sw * acc;
         }
     }
     return ORACLE_OK;

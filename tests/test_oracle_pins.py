@@ -347,6 +347,76 @@ def test_e4m3_tensor_quantize_matches_the_torch_recipe():
     np.testing.assert_allclose(L, ref, rtol=1e-12, atol=1e-12)
 
 
+def _torch_token_recipe(hf: torch.Tensor):
+    """Per-token dynamic E4M3 quantization written with torch ops: float32
+    row amax with a 1e-12 floor, divide by 448, divide, clamp, cast."""
+    fmax = torch.finfo(torch.float8_e4m3fn).max
+    sref = hf.abs().amax(dim=1).clamp_min(1e-12) / fmax
+    qref = (hf / sref[:, None]).clamp(-fmax, fmax).to(torch.float8_e4m3fn)
+    return qref.view(torch.uint8), sref
+
+
+def test_fp8_tokens_quantize_matches_the_torch_recipe():
+    """Bit-exact against the torch recipe, one scale per row: rows of random
+    values, an all-zero row (the 1e-12 floor), signed zeros, a row with one
+    large value among tiny ones (codes that underflow to zero keep their
+    sign), and a row whose scale is a power of two."""
+    rng = np.random.default_rng(11)
+    h = torch.from_numpy(rng.standard_normal((7, 96))).to(torch.bfloat16)
+    h[1] = 0.0
+    h[2, 5] = -0.0
+    h[3] = torch.from_numpy(rng.standard_normal(96) * 1e-6).to(torch.bfloat16)
+    h[3, 0] = 1000.0
+    h[4] = torch.linspace(-3.5, 3.5, 96).to(torch.bfloat16)
+    h[4, 0] = 448.0  # scale exactly 1
+    qx, sx = oracle.fp8_tokens_quantize(_bits(h))
+    qref, sref = _torch_token_recipe(h.float())
+    assert np.array_equal(sx, sref.numpy())
+    assert np.array_equal(qx, qref.numpy())
+    assert sx[1] == np.float32(np.float32(1e-12) / np.float32(448))
+    assert sx[4] == 1.0
+    assert (qx[3] == 0x80).any() and qx[3, 0] == 0x7E
+
+
+def test_fp8_tokens_scale_is_per_row():
+    """Scaling one row of h by a power of two scales its sx by the same
+    factor, leaves its codes unchanged and leaves every other row alone --
+    which a per-tensor scale would not."""
+    rng = np.random.default_rng(12)
+    h = torch.from_numpy(rng.standard_normal((3, 64))).to(torch.bfloat16)
+    q0, s0 = oracle.fp8_tokens_quantize(_bits(h))
+    h2 = h.clone()
+    h2[1] *= 2.0 ** 5
+    q1, s1 = oracle.fp8_tokens_quantize(_bits(h2))
+    assert np.array_equal(q0, q1)
+    assert s1[1] == s0[1] * np.float32(32) and s1[0] == s0[0] and s1[2] == s0[2]
+
+
+def test_w8a8_logits_match_a_float64_matmul():
+    """The W8A8 logits against a float64 torch matmul of both operands
+    decoded through torch's float8_e4m3fn dtype, times sx[b] * sw; and the
+    hand case of one nonzero code on each side."""
+    rng = np.random.default_rng(13)
+    w = torch.from_numpy(rng.standard_normal((128, 80)).astype(np.float32) * 0.02
+                         ).to(torch.bfloat16)
+    q, sw = oracle.e4m3_tensor_quantize(_bits(w), np.arange(128, dtype=np.int32))
+    h = torch.from_numpy(rng.standard_normal((3, 80))).to(torch.bfloat16)
+    qx, sx = oracle.fp8_tokens_quantize(_bits(h))
+    L = oracle.w8a8_logits(q, sw, qx, sx)
+    dw = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64)
+    dx = torch.from_numpy(qx).view(torch.float8_e4m3fn).to(torch.float64)
+    ref = (dx @ dw.T) * torch.from_numpy(sx).double()[:, None] * float(sw)
+    np.testing.assert_allclose(L, ref.numpy(), rtol=1e-12, atol=0)
+    # one code of 2.0 (0x40) in the head against one of -0.5 (0xB0) in the
+    # token at the same k: sx * sw * 2 * -0.5
+    qh = np.zeros((64, 16), dtype=np.uint8)
+    qh[9, 4] = 0x40
+    qt = np.zeros((1, 16), dtype=np.uint8)
+    qt[0, 4] = 0xB0
+    L1 = oracle.w8a8_logits(qh, np.float32(0.25), qt, np.array([8.0], np.float32))
+    assert L1[0, 9] == -2.0 and np.count_nonzero(L1) == 1
+
+
 # ------------------------------------------- readings of silent float steps
 
 def test_block_scale_reading_is_bmax_over_six_gs():
@@ -376,6 +446,18 @@ def test_e4m3_tensor_reading_divides_by_the_scale():
     assert wb.float()[5, 3].item() == 1.1399388313293457e-06
     q, scale = oracle.e4m3_tensor_quantize(_bits(wb), np.arange(64, dtype=np.int32))
     assert q[5, 3] == 26 and q[0, 0] == 0x7E
+
+
+def test_fp8_tokens_reading_divides_by_the_scale():
+    """The per-token quant divides by the row's scale, as page 2's head
+    conversion does.  With amax 4.75, x = -3.5625 gives x / sx = -336
+    exactly, a tie between 320 and 352 that goes to the even code 0xFA;
+    x * (1/sx) is -336.00003 and would give 0xFB."""
+    h = torch.zeros((1, 16), dtype=torch.float32)
+    h[0, 0] = 4.75
+    h[0, 1] = -3.5625
+    qx, sx = oracle.fp8_tokens_quantize(_bits(h.to(torch.bfloat16)))
+    assert qx[0, 1] == 0xFA and qx[0, 0] == 0x7E
 
 
 def test_markstein_quotient_equals_the_division(tmp_path):
