@@ -11,7 +11,8 @@ the timed region (the quantizer is timed separately).
 
 Workloads (reduced_vocab_nvfp4_amd/workloads.py; seeded synthetic inputs):
   flash_next_64k   NVFP4 64 064 x 2560, batch 1, top token  (default)
-  h98k_b16         NVFP4 (or --format e4m3) 98 304 x 2560, batch 16
+  h98k_b16         NVFP4 (or --format e4m3, or w8a8: the E4M3 head with
+                   per-token E4M3 activations) 98 304 x 2560, batch 16
   dense27b_64k_b8  NVFP4 64 064 x 5120, batch 8, fp32 logits to 248 320 ids
   stock_bf16       BF16 248 320 x 2560 (every id), batch 1, top token
   tiny             NVFP4 1024 x 256, batch 1 (launch-bound; correctness)
@@ -67,14 +68,15 @@ RTOL, ATOL = 1e-3, 1e-4
 
 def weight_bytes(fmt, n_rows, hidden):
     return {"nvfp4": n_rows * hidden // 2 + n_rows * hidden // 16,
-            "e4m3": n_rows * hidden,
+            "e4m3": n_rows * hidden, "w8a8": n_rows * hidden,
             "bf16": n_rows * hidden * 2}[fmt]
 
 
 def algorithmic_bytes(fmt, n_rows, hidden, batch, op, vocab):
     """Bytes a step must move: the head (codes and scales), h, the tensor
     scale, then either the winning dh_idx entries and the out ids, or the
-    dh_idx column and the full fp32 logits."""
+    dh_idx column and the full fp32 logits.  (The W8A8 step's quantized
+    tokens are an intermediate, not counted.)"""
     b = weight_bytes(fmt, n_rows, hidden) + batch * hidden * 2
     b += 4 if fmt != "bf16" else 0
     if op == "logits":
@@ -146,7 +148,9 @@ class Case:
         self.idx = idx.numpy()
         self.n_rows = idx.shape[0]
         self.idx_gpu = idx.to(dev)
-        self.ws = dh.new_workspace(self.n_rows, self.B, dev)
+        self.ws = (dh.new_workspace_w8a8(self.n_rows, self.B, self.H, dev)
+                   if fmt == "w8a8" else
+                   dh.new_workspace(self.n_rows, self.B, dev))
         w_gpu = self.w.to(dev)
         self.quant_us = None
         if fmt == "nvfp4":
@@ -156,7 +160,7 @@ class Case:
                 w_gpu, self.idx_gpu, packed=packed, scales=scales,
                 global_scale=self.scale, workspace=self.ws)
             tensors = (packed, scales)
-        elif fmt == "e4m3":
+        elif fmt in ("e4m3", "w8a8"):
             q, self.scale = dh.e4m3_quantize_rows_per_tensor(
                 w_gpu, self.idx_gpu, workspace=self.ws)
             quant = lambda: dh.e4m3_quantize_rows_per_tensor(  # noqa: E731
@@ -221,6 +225,11 @@ class Case:
                     return L.draft_head_logits_e4m3(hd[0], sc, idx_p, n, nk,
                                                     H, V, hp, B, o, ws_p,
                                                     ws_n, sp)
+            elif fmt == "w8a8":
+                def lcall(hd, hp, o):
+                    return L.draft_head_logits_w8a8(hd[0], sc, idx_p, n, nk,
+                                                    H, V, hp, B, o, ws_p,
+                                                    ws_n, sp)
             else:
                 def lcall(hd, hp, o):
                     return L.draft_head_logits_bf16(hd[0], idx_p, n, nk, H, V,
@@ -240,6 +249,10 @@ class Case:
             def call(hd, hp, o):
                 return L.draft_head_top_tokens_e4m3(hd[0], sc, idx_p, n, H,
                                                     hp, B, o, ws_p, ws_n, sp)
+        elif fmt == "w8a8":
+            def call(hd, hp, o):
+                return L.draft_head_top_tokens_w8a8(hd[0], sc, idx_p, n, H,
+                                                    hp, B, o, ws_p, ws_n, sp)
         else:
             def call(hd, hp, o):
                 return L.draft_head_top_tokens_bf16(hd[0], idx_p, n, H, hp,
@@ -258,7 +271,7 @@ class Case:
         t0 = time.perf_counter()
         if self.fmt == "nvfp4":
             self.o_head = oracle.nvfp4_quantize(bits, self.idx)
-        elif self.fmt == "e4m3":
+        elif self.fmt in ("e4m3", "w8a8"):
             self.o_head = oracle.e4m3_tensor_quantize(bits, self.idx)
         else:
             self.o_head = bits
@@ -271,6 +284,9 @@ class Case:
             L = oracle.nvfp4_logits(*self.o_head, hb)
         elif self.fmt == "e4m3":
             L = oracle.e4m3_tensor_logits(*self.o_head, hb)
+        elif self.fmt == "w8a8":
+            L = oracle.w8a8_logits(*self.o_head,
+                                   *oracle.fp8_tokens_quantize(hb))
         else:
             L = oracle.bf16_logits(self.o_head, self.idx, hb)
         if self.op == "logits":
@@ -367,7 +383,7 @@ def main():
     ap.add_argument("--config", default="flash_next_64k",
                     choices=sorted(wl.WORKLOADS))
     ap.add_argument("--format", default=None,
-                    choices=["nvfp4", "e4m3", "bf16"],
+                    choices=["nvfp4", "e4m3", "w8a8", "bf16"],
                     help="head format (default: the workload's first)")
     ap.add_argument("--op", default=None, choices=["top", "logits"],
                     help="step kind of a head workload (default: logits for "
@@ -500,7 +516,7 @@ def main():
             "workload": case.name, "vocab": V, "hidden": H, "batch": B,
             "n_rows": case.n_rows, "n_kept": case.n_kept,
             "format": {"nvfp4": "nvfp4-w4a16", "e4m3": "e4m3-w8a16",
-                       "bf16": "bf16"}[fmt],
+                       "w8a8": "e4m3-w8a8", "bf16": "bf16"}[fmt],
             "step": {"top": "top tokens",
                      "logits": "fp32 logits to the full vocab",
                      "linear": "NVFP4 W4A16 linear, fp32 out"}[case.op],
@@ -514,7 +530,8 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": load_traffic(case.name, khash),
             "bytes_per_step": case.nbytes,
-            "launches_per_step": 2 if case.op == "logits" else 1,
+            "launches_per_step": ((2 if case.op == "logits" else 1)
+                                  + (1 if fmt == "w8a8" else 0)),
         },
         "cpu_baseline": result_cpu,
         "parity": parity,

@@ -67,7 +67,7 @@ extern "C" {
 #define DH_EWORKSPACE (-2) /* workspace pointer null or too small */
 #define DH_EHIP (-3)       /* a HIP runtime call or kernel launch failed */
 
-#define DRAFTHEAD_ABI_VERSION 1
+#define DRAFTHEAD_ABI_VERSION 2
 
 int drafthead_abi_version(void);
 
@@ -211,6 +211,61 @@ int draft_head_top_tokens_e4m3(const uint8_t* q, const float* scale,
  * Errors: as draft_head_logits.
  */
 int draft_head_logits_e4m3(const uint8_t* q, const float* scale,
+                           const int32_t* dh_idx, int64_t n_rows,
+                           int64_t n_kept, int64_t hidden, int64_t vocab,
+                           const void* h_bf16, int64_t batch,
+                           float* out_logits, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Per-token dynamic E4M3 quantization of hidden states (page 2, "FP8 MTP
+ * draft stack for vLLM", _Fp8DraftHeadMethod.apply: the FP8 head quantizes
+ * each token's activations with a scale of its own before the scaled GEMM).
+ *   h_bf16 [device] batch x hidden BF16, 16-byte aligned
+ *   qx     [device] out: batch x hidden e4m3fn bytes, 8-byte aligned
+ *   sx     [device] out: batch float32 scales
+ * Arithmetic (float32, round-to-nearest-even), per row b: amax over the
+ * row; sx[b] = max(amax, 1e-12) / 448; qx = e4m3(clamp(x / sx[b], -448,
+ * 448)), sign kept -- the head's recipe with one scale per token.
+ * Errors: DH_EINVAL for a null or misaligned pointer, hidden not a multiple
+ * of 16 in [16, 16384], batch < 1 or > 65536; DH_EHIP.
+ */
+int fp8_quantize_tokens(const void* h_bf16, int64_t batch, int64_t hidden,
+                        uint8_t* qx, float* sx, void* stream);
+
+/* Workspace bytes for the W8A8 head calls below (0 for an invalid shape):
+ * the top-token workspace plus room for the quantized tokens. */
+size_t draft_head_workspace_bytes_w8a8(int64_t n_rows, int64_t batch,
+                                       int64_t hidden);
+
+/*
+ * Greedy draft tokens of the FP8 head as page 2 applies it, W8A8 (page 2,
+ * _Fp8DraftHeadMethod.apply: per-token dynamic activation quantization,
+ * then a GEMM scaled by the token's and the head's scale; page 1,
+ * get_top_tokens for the argmax and the remap).  q and scale come from
+ * e4m3_quantize_rows_per_tensor.  The call quantizes h as
+ * fp8_quantize_tokens does, into the workspace, then
+ * logit_j = sum_k e4m3(q[j,k]) * e4m3(qx[b,k]) in float32 (each product is
+ * exact); the scales are positive and leave the argmax unchanged.
+ * out_ids[b] = dh_idx[lowest j with the largest logit].
+ *   workspace  zero-filled once, draft_head_workspace_bytes_w8a8 bytes; it
+ *              carries state from call to call as for draft_head_top_tokens
+ * Errors: as draft_head_top_tokens.
+ */
+int draft_head_top_tokens_w8a8(const uint8_t* q, const float* scale,
+                               const int32_t* dh_idx, int64_t n_rows,
+                               int64_t hidden, const void* h_bf16,
+                               int64_t batch, int32_t* out_ids,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Logits of the W8A8 FP8 head (page 2, apply and compute_logits): as
+ * draft_head_logits with
+ * out[b, dh_idx[j]] = sx[b] * scale * sum_k e4m3(q[j,k]) * e4m3(qx[b,k]).
+ * Errors: as draft_head_logits; the workspace as above.
+ */
+int draft_head_logits_w8a8(const uint8_t* q, const float* scale,
                            const int32_t* dh_idx, int64_t n_rows,
                            int64_t n_kept, int64_t hidden, int64_t vocab,
                            const void* h_bf16, int64_t batch,

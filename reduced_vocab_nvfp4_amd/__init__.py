@@ -85,6 +85,19 @@ def lib() -> ctypes.CDLL:
         L.draft_head_logits_e4m3.argtypes = [
             _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64, _c_ptr,
             _c_i64, _c_ptr, _c_ptr, _c_size, _c_ptr]
+        L.fp8_quantize_tokens.restype = ctypes.c_int
+        L.fp8_quantize_tokens.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr,
+                                          _c_ptr, _c_ptr]
+        L.draft_head_workspace_bytes_w8a8.restype = _c_size
+        L.draft_head_workspace_bytes_w8a8.argtypes = [_c_i64, _c_i64, _c_i64]
+        L.draft_head_top_tokens_w8a8.restype = ctypes.c_int
+        L.draft_head_top_tokens_w8a8.argtypes = [
+            _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
+            _c_ptr, _c_size, _c_ptr]
+        L.draft_head_logits_w8a8.restype = ctypes.c_int
+        L.draft_head_logits_w8a8.argtypes = [
+            _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64, _c_ptr,
+            _c_i64, _c_ptr, _c_ptr, _c_size, _c_ptr]
         L.draft_head_top_tokens_bf16.restype = ctypes.c_int
         L.draft_head_top_tokens_bf16.argtypes = [
             _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr,
@@ -316,6 +329,80 @@ def draft_head_logits_e4m3(q, scale, dh_idx, n_kept: int, vocab: int, h, *,
     return out
 
 
+# ------------------------------------------------- W8A8 (FP8) head, page 2
+
+def fp8_quantize_tokens(h, *, qx=None, sx=None, stream=None):
+    """Per-token dynamic E4M3 quantization of BF16 h [B, H]:
+    (qx uint8 [B, H] e4m3fn codes, sx float32 [B] scales)."""
+    B, H = h.shape
+    dev = h.device
+    if qx is None:
+        qx = torch.empty((B, H), dtype=torch.uint8, device=dev)
+    if sx is None:
+        sx = torch.empty(B, dtype=torch.float32, device=dev)
+    rc = lib().fp8_quantize_tokens(
+        _dev(h, "h", torch.bfloat16), B, H, _dev(qx, "qx", torch.uint8),
+        _dev(sx, "sx", torch.float32), _stream(dev, stream))
+    _check("fp8_quantize_tokens", rc)
+    return qx, sx
+
+
+def draft_head_workspace_bytes_w8a8(n_rows: int, batch: int,
+                                    hidden: int) -> int:
+    return int(lib().draft_head_workspace_bytes_w8a8(n_rows, batch, hidden))
+
+
+def new_workspace_w8a8(n_rows: int, batch: int, hidden: int,
+                       device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for the W8A8 head calls."""
+    n = draft_head_workspace_bytes_w8a8(n_rows, batch, hidden)
+    if n == 0:
+        raise ValueError("invalid n_rows/batch/hidden for a workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def draft_head_top_tokens_w8a8(q, scale, dh_idx, h, *, out_ids=None,
+                               workspace=None, stream=None):
+    """Greedy draft tokens of an E4M3 head applied W8A8 (the tokens are
+    quantized per token inside the call): int32 [B] target ids."""
+    n, H = q.shape
+    B = h.shape[0]
+    dev = h.device
+    if out_ids is None:
+        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace_w8a8(n, B, H, dev)
+    rc = lib().draft_head_top_tokens_w8a8(
+        _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, H,
+        _dev(h, "h", torch.bfloat16), B, _dev(out_ids, "out_ids", torch.int32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_top_tokens_w8a8", rc)
+    return out_ids
+
+
+def draft_head_logits_w8a8(q, scale, dh_idx, n_kept: int, vocab: int, h, *,
+                           out=None, workspace=None, stream=None):
+    """float32 [B, vocab] W8A8 logits of an E4M3 head, -inf at ids not
+    kept."""
+    n, H = q.shape
+    B = h.shape[0]
+    dev = h.device
+    if out is None:
+        out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = new_workspace_w8a8(n, B, H, dev)
+    rc = lib().draft_head_logits_w8a8(
+        _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, int(n_kept), H, int(vocab),
+        _dev(h, "h", torch.bfloat16), B, _dev(out, "out", torch.float32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_logits_w8a8", rc)
+    return out
+
+
 # ------------------------------------------------------- BF16 (stock) head
 
 def draft_head_top_tokens_bf16(w, dh_idx, h, *, out_ids=None, workspace=None,
@@ -363,6 +450,8 @@ __all__ = [
     "draft_head_workspace_bytes", "new_workspace", "nvfp4_quantize_rows",
     "draft_head_top_tokens", "draft_head_logits", "nvfp4_linear",
     "e4m3_quantize_rows_per_tensor", "draft_head_top_tokens_e4m3",
-    "draft_head_logits_e4m3", "draft_head_top_tokens_bf16",
-    "draft_head_logits_bf16",
+    "draft_head_logits_e4m3", "fp8_quantize_tokens",
+    "draft_head_workspace_bytes_w8a8", "new_workspace_w8a8",
+    "draft_head_top_tokens_w8a8", "draft_head_logits_w8a8",
+    "draft_head_top_tokens_bf16", "draft_head_logits_bf16",
 ]

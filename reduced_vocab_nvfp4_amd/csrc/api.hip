@@ -119,6 +119,73 @@ static int logits(int fmt, const void* w, const uint8_t* scales,
   return status(launch_gemv(a, static_cast<hipStream_t>(stream)));
 }
 
+// W8A8 workspace: the GEMV's own workspace, then the tokens' activations
+// (the BF16 values of their E4M3 codes, [batch][hidden]) and their scales.
+// total == 0 for an invalid shape.
+struct W8a8Layout {
+  size_t act, sx, total;
+};
+
+static W8a8Layout w8a8_layout(int64_t n_rows, int64_t batch, int64_t hidden) {
+  W8a8Layout l{};
+  const size_t base = workspace_bytes(n_rows, batch);
+  if (base == 0 || hidden < 16 || hidden > 16384 || hidden % 16 != 0)
+    return l;
+  l.act = (base + 255) / 256 * 256;
+  l.sx = l.act + ((size_t)batch * (size_t)hidden * 2 + 255) / 256 * 256;
+  l.total = l.sx + ((size_t)batch * 4 + 255) / 256 * 256;
+  return l;
+}
+
+// The FP8 head's step: per-token E4M3 quantization of h into the
+// workspace, then the E4M3 GEMV on the tokens' exact BF16 values (each
+// product is a product of two E4M3 values, as in an FP8 GEMM).  The logits
+// carry each token's scale; the top token does not need it (a positive
+// factor per batch row leaves the row's argmax unchanged).
+static int w8a8(const uint8_t* q, const float* scale, const int32_t* dh_idx,
+                int64_t n_rows, int64_t n_kept, int64_t hidden, int64_t vocab,
+                const void* h, int64_t batch, int32_t* out_ids, float* out,
+                void* ws, size_t ws_bytes, void* stream) {
+  if (out_ids) {
+    if (!aligned(out_ids, 4)) return DH_EINVAL;
+  } else {
+    if (!out || !aligned(out, 16)) return DH_EINVAL;
+    if (n_kept < 1 || n_kept > n_rows || vocab < n_kept || vocab > INT32_MAX)
+      return DH_EINVAL;
+  }
+  const int rc = check_head(FMT_E4M3, q, nullptr, scale, dh_idx, n_rows,
+                            hidden, h, batch, ws, ws_bytes);
+  if (rc != DH_OK) return rc;
+  const W8a8Layout l = w8a8_layout(n_rows, batch, hidden);
+  if (ws_bytes < l.total) return DH_EWORKSPACE;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  uint16_t* hq = reinterpret_cast<uint16_t*>(wsb + l.act);
+  float* sx = reinterpret_cast<float*>(wsb + l.sx);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = launch_fp8_tokens(static_cast<const uint16_t*>(h),
+                                         batch, hidden, nullptr, hq, sx, s);
+  if (e != hipSuccess) return DH_EHIP;
+  GemvArgs a{};
+  a.fmt = FMT_E4M3;
+  a.w = q;
+  a.scale = scale;
+  a.dh_idx = dh_idx;
+  a.n_rows = n_rows;
+  a.hidden = hidden;
+  a.h = hq;
+  a.batch = batch;
+  a.ws = wsb;
+  if (out_ids) {
+    a.out_ids = out_ids;
+  } else {
+    a.out_logits = out;
+    a.n_kept = n_kept;
+    a.vocab = vocab;
+    a.row_scale = sx;
+  }
+  return status(launch_gemv(a, s));
+}
+
 // Checks shared by the quantizers.
 static int check_quant(const void* w, int64_t vocab, int64_t hidden,
                        const int32_t* ids, int64_t n_rows, const void* out,
@@ -288,6 +355,46 @@ int draft_head_logits_e4m3(const uint8_t* q, const float* scale,
   return dh::logits(dh::FMT_E4M3, q, nullptr, scale, dh_idx, n_rows, n_kept,
                     hidden, vocab, h_bf16, batch, out_logits, workspace,
                     workspace_bytes, stream);
+}
+
+size_t draft_head_workspace_bytes_w8a8(int64_t n_rows, int64_t batch,
+                                       int64_t hidden) {
+  return dh::w8a8_layout(n_rows, batch, hidden).total;
+}
+
+int fp8_quantize_tokens(const void* h_bf16, int64_t batch, int64_t hidden,
+                        uint8_t* qx, float* sx, void* stream) {
+  using namespace dh;
+  if (!h_bf16 || !qx || !sx) return DH_EINVAL;
+  if (!aligned(h_bf16, 16) || !aligned(qx, 8) || !aligned(sx, 4))
+    return DH_EINVAL;
+  if (hidden < 16 || hidden > 16384 || hidden % 16 != 0) return DH_EINVAL;
+  if (batch < 1 || batch > MAX_TOKENS) return DH_EINVAL;
+  return status(launch_fp8_tokens(static_cast<const uint16_t*>(h_bf16), batch,
+                                  hidden, qx, nullptr, sx,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int draft_head_top_tokens_w8a8(const uint8_t* q, const float* scale,
+                               const int32_t* dh_idx, int64_t n_rows,
+                               int64_t hidden, const void* h_bf16,
+                               int64_t batch, int32_t* out_ids,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!out_ids) return DH_EINVAL;
+  return dh::w8a8(q, scale, dh_idx, n_rows, 0, hidden, 0, h_bf16, batch,
+                  out_ids, nullptr, workspace, workspace_bytes, stream);
+}
+
+int draft_head_logits_w8a8(const uint8_t* q, const float* scale,
+                           const int32_t* dh_idx, int64_t n_rows,
+                           int64_t n_kept, int64_t hidden, int64_t vocab,
+                           const void* h_bf16, int64_t batch,
+                           float* out_logits, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return dh::w8a8(q, scale, dh_idx, n_rows, n_kept, hidden, vocab, h_bf16,
+                  batch, nullptr, out_logits, workspace, workspace_bytes,
+                  stream);
 }
 
 int draft_head_top_tokens_bf16(const void* w_bf16, const int32_t* dh_idx,

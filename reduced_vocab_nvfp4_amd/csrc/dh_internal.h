@@ -20,6 +20,7 @@ constexpr size_t WS_SLOTS = 256;
 constexpr int MAX_GRID = 4096;  // upper bound of any argmax grid
 constexpr int MAX_BATCH = 64;
 constexpr int MAX_SLICE = 16;   // batch rows per kernel launch
+constexpr int64_t MAX_TOKENS = 1 << 16;  // rows of one token quantization
 
 size_t workspace_bytes(int64_t n_rows, int64_t batch);
 
@@ -53,6 +54,12 @@ struct QuantE4m3Args {
 };
 hipError_t launch_e4m3_quantize(const QuantE4m3Args& a, hipStream_t s);
 
+// Per-token E4M3 quantization of h [batch][hidden] (hidden % 8 == 0): codes
+// to qx, their exact BF16 values to hq (either may be null), scales to sx.
+hipError_t launch_fp8_tokens(const uint16_t* h, int64_t batch, int64_t hidden,
+                             uint8_t* qx, uint16_t* hq, float* sx,
+                             hipStream_t s);
+
 // One GEMV call: weight format (WeightFormat in formats.h), the head, h and
 // either out_ids (top tokens) or out_logits (logits scatter).
 struct GemvArgs {
@@ -71,6 +78,9 @@ struct GemvArgs {
   // Dense output (the linear): out_logits[b][j] for every row j, no index,
   // no -inf fill; dh_idx, n_kept and vocab are ignored.
   bool dense = false;
+  // Logits only: one more factor per batch row (the W8A8 head's token
+  // scales), null for none.
+  const float* row_scale = nullptr;
 };
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
 

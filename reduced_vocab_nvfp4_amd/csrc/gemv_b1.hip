@@ -181,7 +181,7 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
       hreg[i * HD + 4 * q + 3] = v.w;
     }
   }
-  const float sc = LOGITS ? tensor_scale(a) : 1.0f;
+  const float sc = LOGITS ? logit_scale(a, 0) : 1.0f;
   float best_v = -INFINITY;
   int best_r = INT_MAX;
 

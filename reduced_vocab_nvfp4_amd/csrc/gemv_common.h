@@ -48,6 +48,7 @@ struct KArgs {
   int64_t n_kept, vocab;  // dense mode: n_kept = n_rows, vocab = row stride
   uint8_t* ws;
   int ks_log2;  // MFMA dense mode: log2 of the waves that share a unit
+  const float* row_scale;  // logits: factor of batch row b (slice), or null
 };
 
 // Kernel descriptor used by the dispatcher.
@@ -82,6 +83,13 @@ __device__ __forceinline__ uint64_t pack_partial(float v, int r) {
 
 __device__ __forceinline__ float tensor_scale(const KArgs& a) {
   return a.scale ? *a.scale : 1.0f;
+}
+
+// The logits factor of batch row m of the slice: the tensor scale times the
+// row's own scale when there is one (m < nb).
+__device__ __forceinline__ float logit_scale(const KArgs& a, int m) {
+  const float s = tensor_scale(a);
+  return a.row_scale ? s * a.row_scale[m] : s;
 }
 
 // Call counter of the argmax slots.  The workspace keeps it; a call's

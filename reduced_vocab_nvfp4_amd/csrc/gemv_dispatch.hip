@@ -127,6 +127,7 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     k.vocab = cols;
     k.ws = ga.ws;
     k.ks_log2 = kl;
+    k.row_scale = ga.row_scale ? ga.row_scale + b0 : nullptr;
     void* kargs[] = {&k};
     e = hipLaunchKernel(d.fn, dim3((unsigned)grid), dim3(d.threads), kargs,
                         d.lds_bytes, s);

@@ -55,7 +55,8 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
       const float v = group_sum<64>(acc[b]);
       if constexpr (LOGITS) {
         if (lane == 0 && row < a.n_kept)
-          a.out_logits[b * a.vocab + out_col<MODE>(a.dh_idx, row)] = v * sc;
+          a.out_logits[b * a.vocab + out_col<MODE>(a.dh_idx, row)] =
+              v * (a.row_scale ? sc * a.row_scale[b] : sc);
       } else if (v > best_v[b]) {
         best_v[b] = v;
         best_r[b] = (int)row;

@@ -208,7 +208,12 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   f32x4 acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const float sc = LOGITS ? tensor_scale(a) : 1.0f;
+  // logits factor of batch row 4q + j (rows past the slice are never
+  // written)
+  float lsc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    lsc[j] = LOGITS && 4 * q + j < nb ? logit_scale(a, 4 * q + j) : 1.0f;
   float best_v[4];
   int best_r[4];
 #pragma unroll
@@ -291,7 +296,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
                 const int m = 4 * q + j;
                 if (m < nb && row < a.n_kept)
                   a.out_logits[(int64_t)m * a.vocab +
-                               (MODE == OUT_DENSE ? row : b.ids[t])] = v * sc;
+                               (MODE == OUT_DENSE ? row : b.ids[t])] =
+                      v * lsc[j];
               } else if (v > best_v[j]) {
                 // a lane's rows ascend: strict > keeps the lowest
                 best_v[j] = v;
@@ -330,7 +336,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int m = 4 * q + j;
-            if (m < nb) a.out_logits[(int64_t)m * a.vocab + row] = v[j] * sc;
+            if (m < nb)
+              a.out_logits[(int64_t)m * a.vocab + row] = v[j] * lsc[j];
           }
         }
       }

@@ -356,6 +356,72 @@ __global__ void k_quant_finish(uint32_t* __restrict__ amax_bits,
   }
 }
 
+// Per-token dynamic E4M3 activations: one block per row of h.  The row's
+// scale is max(amax, 1e-12)/448, the head's recipe with one scale per token;
+// each element is x / scale (an IEEE division: a row has at most 16 384),
+// clamped to +-448 and converted in hardware, which is exact there.  The
+// codes go to qx and, decoded back to BF16 (exact: every E4M3 value is a
+// BF16 value), to hq, the activations the GEMV kernels read.  Either output
+// may be null.
+__global__ __launch_bounds__(QTHREADS) void k_fp8_tokens(
+    const uint16_t* __restrict__ h, int64_t hidden, uint8_t* __restrict__ qx,
+    uint16_t* __restrict__ hq, float* __restrict__ sx) {
+  __shared__ uint32_t red[QWAVES];
+  const int64_t b = blockIdx.x;
+  const uint4* row = reinterpret_cast<const uint4*>(h + b * hidden);
+  const int n8 = (int)(hidden / 8);
+  uint32_t m = 0u;
+  for (int i = threadIdx.x; i < n8; i += QTHREADS) {
+    const uint32_t v = abs_bf16_max8(row[i]);
+    m = v > m ? v : m;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+    m = o > m ? o : m;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < QWAVES; ++w) m = red[w] > m ? red[w] : m;
+  // magnitudes are compared as bf16 bit patterns (monotonic for |x|)
+  const float scale = fmaxf(bf16_to_f32(m), 1e-12f) / 448.0f;
+  for (int i = threadIdx.x; i < n8; i += QTHREADS) {
+    const uint4 v = row[i];
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t code[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float t[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t bits = (x[(e + k) >> 1] >> (((e + k) & 1) * 16)) &
+                              0xFFFFu;
+        t[k] = fminf(fmaxf(bf16_to_f32(bits) / scale, -448.0f), 448.0f);
+      }
+      code[e >> 2] |= fp8_pair(t[0], t[1]) << ((e & 2) * 8);
+    }
+    if (qx)
+      *reinterpret_cast<uint2*>(qx + b * hidden + 8 * i) =
+          make_uint2(code[0], code[1]);
+    if (hq) {
+      // each call decodes the low (false) or high (true) pair of a word
+      const uint32_t d0 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code[0], 1.0f, false));
+      const uint32_t d1 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code[0], 1.0f, true));
+      const uint32_t d2 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code[1], 1.0f, false));
+      const uint32_t d3 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code[1], 1.0f, true));
+      *reinterpret_cast<uint4*>(hq + b * hidden + 8 * i) =
+          make_uint4(d0, d1, d2, d3);
+    }
+  }
+  if (threadIdx.x == 0) sx[b] = scale;
+}
+
 // Blocks for n_rows gathered rows: one wave per tile, at most 8 blocks of
 // 4 waves per CU (one resident round at the kernels' register use).
 int grid_for(int64_t n_rows, int64_t hidden, int cus) {
@@ -379,6 +445,13 @@ hipError_t launch_nvfp4_quantize(const QuantArgs& a, hipStream_t s) {
   k_nvfp4_encode<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
                                            amax, a.packed, a.scales);
   k_quant_finish<false><<<1, 64, 0, s>>>(amax, a.global_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_tokens(const uint16_t* h, int64_t batch, int64_t hidden,
+                             uint8_t* qx, uint16_t* hq, float* sx,
+                             hipStream_t s) {
+  k_fp8_tokens<<<(unsigned)batch, QTHREADS, 0, s>>>(h, hidden, qx, hq, sx);
   return hipGetLastError();
 }
 

@@ -85,8 +85,9 @@ WORKLOADS = {
         note="NVFP4 W4A16 linear, 5120 outputs from 2560 inputs, B=16 (MFMA)"),
     "h98k_b16": Workload(
         "h98k_b16", vocab=248320, hidden=2560, batch=16, n_keep=98304,
-        forced_tail=256, formats=("nvfp4", "e4m3"),
-        note="V=248320 H=2560, 98304 kept, NVFP4 and E4M3 per-tensor, B=16"),
+        forced_tail=256, formats=("nvfp4", "e4m3", "w8a8"),
+        note="V=248320 H=2560, 98304 kept, NVFP4 and E4M3 per-tensor "
+             "(W8A16, or W8A8 with per-token E4M3 activations), B=16"),
 }
 
 

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(dh.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared but not exported"
-    assert dh.lib().drafthead_abi_version() == 1
+    assert dh.lib().drafthead_abi_version() == 2
     assert dh.error_string(dh.DH_EINVAL).startswith("invalid")
 
 
@@ -218,3 +218,69 @@ def test_linear_rejects_bad_arguments_on_the_host():
     assert lin(p=FAKE + 8) == dh.DH_EINVAL   # 16-byte alignment
     assert lin(out=FAKE + 4) == dh.DH_EINVAL
     assert lin(g=FAKE + 2) == dh.DH_EINVAL
+
+
+def test_token_quantize_rejects_bad_arguments_on_the_host():
+    L = dh.lib()
+    base = dict(h=FAKE, B=4, H=256, qx=FAKE, sx=FAKE)
+
+    def tq(**kw):
+        a = {**base, **kw}
+        return L.fp8_quantize_tokens(a["h"], a["B"], a["H"], a["qx"], a["sx"],
+                                     None)
+    assert tq(h=None) == dh.DH_EINVAL
+    assert tq(qx=None) == dh.DH_EINVAL
+    assert tq(sx=None) == dh.DH_EINVAL
+    assert tq(B=0) == dh.DH_EINVAL
+    assert tq(B=65537) == dh.DH_EINVAL
+    assert tq(H=8) == dh.DH_EINVAL
+    assert tq(H=40) == dh.DH_EINVAL
+    assert tq(H=16400) == dh.DH_EINVAL
+    assert tq(h=FAKE + 8) == dh.DH_EINVAL    # 16-byte alignment
+    assert tq(qx=FAKE + 4) == dh.DH_EINVAL   # 8-byte alignment
+    assert tq(sx=FAKE + 2) == dh.DH_EINVAL
+
+
+def test_w8a8_workspace_and_arguments_on_the_host():
+    """The W8A8 workspace is the top-token workspace plus the tokens' BF16
+    activations and scales; every call checks it on the host."""
+    base = dh.draft_head_workspace_bytes(98304, 16)
+    w = dh.draft_head_workspace_bytes_w8a8(98304, 16, 2560)
+    assert w >= base + 16 * 2560 * 2 + 16 * 4
+    assert dh.draft_head_workspace_bytes_w8a8(98304, 16, 5120) > w
+    assert dh.draft_head_workspace_bytes_w8a8(98304, 16, 40) == 0
+    assert dh.draft_head_workspace_bytes_w8a8(0, 16, 2560) == 0
+    assert dh.draft_head_workspace_bytes_w8a8(128, 65, 2560) == 0
+    L = dh.lib()
+    n, H, B = 128, 256, 4
+    need = dh.draft_head_workspace_bytes_w8a8(n, B, H)
+    args = dict(q=FAKE, s=FAKE, idx=FAKE, n=n, H=H, h=FAKE, B=B, out=FAKE,
+                ws=FAKE, wsn=need)
+
+    def top(**kw):
+        a = {**args, **kw}
+        return L.draft_head_top_tokens_w8a8(
+            a["q"], a["s"], a["idx"], a["n"], a["H"], a["h"], a["B"], a["out"],
+            a["ws"], a["wsn"], None)
+
+    def lg(**kw):
+        a = {**args, **kw}
+        return L.draft_head_logits_w8a8(
+            a["q"], a["s"], a["idx"], a["n"], a.get("nk", n), a["H"],
+            a.get("V", 4096), a["h"], a["B"], a["out"], a["ws"], a["wsn"],
+            None)
+    for f in (top, lg):
+        assert f(q=None) == dh.DH_EINVAL
+        assert f(s=None) == dh.DH_EINVAL
+        assert f(out=None) == dh.DH_EINVAL
+        assert f(n=100) == dh.DH_EINVAL
+        assert f(H=40) == dh.DH_EINVAL
+        assert f(B=65) == dh.DH_EINVAL
+        assert f(ws=None) == dh.DH_EWORKSPACE
+        # big enough for the top-token workspace, not for the tokens
+        assert f(wsn=dh.draft_head_workspace_bytes(n, B)) == dh.DH_EWORKSPACE
+        assert f(wsn=need - 1) == dh.DH_EWORKSPACE
+    assert lg(nk=0) == dh.DH_EINVAL
+    assert lg(nk=n + 1) == dh.DH_EINVAL
+    assert lg(V=64) == dh.DH_EINVAL
+    assert lg(out=FAKE + 4) == dh.DH_EINVAL
