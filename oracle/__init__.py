@@ -79,6 +79,15 @@ def lib() -> ctypes.CDLL:
                                                  c_ptr]
         L.oracle_w8a8_logits.argtypes = [c_ptr, ctypes.c_float, c_i64, c_i64,
                                          c_ptr, c_ptr, c_i64, c_ptr]
+        L.oracle_f16_value.restype = ctypes.c_float
+        L.oracle_f16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_code.restype = ctypes.c_uint16
+        L.oracle_bf16_code.argtypes = [ctypes.c_float]
+        L.oracle_nvfp4_quantize_f16.argtypes = [c_ptr, c_i64, c_i64, c_ptr,
+                                                c_i64, c_ptr, c_ptr, c_ptr]
+        L.oracle_logits_to_bf16.argtypes = [c_ptr, c_i64, c_ptr]
+        L.oracle_logits_scatter_bf16.argtypes = [c_ptr, c_i64, c_i64, c_i64,
+                                                 c_ptr, c_i64, c_ptr]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -250,6 +259,59 @@ def w8a8_logits(q: np.ndarray, sw, qx: np.ndarray,
     _check(lib().oracle_w8a8_logits(_p(q), float(sw), n, H, _p(qx), _p(sx),
                                     B, _p(L)), "w8a8_logits")
     return L
+
+
+def f16_value(bits: int) -> float:
+    return float(lib().oracle_f16_value(int(bits)))
+
+
+def bf16_code(x: float) -> int:
+    """C12: BF16 bits of a float32, round to nearest, ties to even."""
+    return int(lib().oracle_bf16_code(float(x)))
+
+
+def nvfp4_quantize_f16(w_bits: np.ndarray, idx: np.ndarray):
+    """C12: NVFP4 quantization of an FP16 head (binary16 bits)."""
+    w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    V, H = w_bits.shape
+    n = idx.shape[0]
+    packed = np.zeros((n, H // 2), dtype=np.uint8)
+    scales = np.zeros((n, H // 16), dtype=np.uint8)
+    gs = np.zeros(1, dtype=np.float32)
+    _check(lib().oracle_nvfp4_quantize_f16(_p(w_bits), V, H, _p(idx), n,
+                                           _p(packed), _p(scales), _p(gs)),
+           "nvfp4_quantize_f16")
+    return packed, scales, np.float32(gs[0])
+
+
+def logits_to_bf16(L: np.ndarray) -> np.ndarray:
+    """C12: BF16 bits (uint16) of float64 logits rounded to float32, then
+    to BF16."""
+    L = np.ascontiguousarray(L, dtype=np.float64)
+    out = np.empty(L.shape, dtype=np.uint16)
+    _check(lib().oracle_logits_to_bf16(_p(L), L.size, _p(out)),
+           "logits_to_bf16")
+    return out
+
+
+def bf16_bits_value(bits: np.ndarray) -> np.ndarray:
+    """float64 values of BF16 bit patterns (the upper half of a float32)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def logits_scatter_bf16(Lb: np.ndarray, n_kept: int, idx: np.ndarray,
+                        vocab: int) -> np.ndarray:
+    """C12: BF16 bits [B, vocab], 0xFF80 (-inf) at ids not kept."""
+    Lb = np.ascontiguousarray(np.atleast_2d(Lb), dtype=np.uint16)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    B, n = Lb.shape
+    out = np.empty((B, vocab), dtype=np.uint16)
+    _check(lib().oracle_logits_scatter_bf16(_p(Lb), B, n, int(n_kept),
+                                            _p(idx), int(vocab), _p(out)),
+           "logits_scatter_bf16")
+    return out
 
 
 def num_threads() -> int:

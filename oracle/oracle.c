@@ -34,6 +34,12 @@
  *   C11 W8A8 logits: both operands E4M3, scaled by the token's and the
  *       head's scale, accumulated in float64              -- page 2,
  *       _Fp8DraftHeadMethod.apply (the scaled GEMM)
+ *   C12 reference-compatible mode: an FP16 head is accepted (its values
+ *       decoded exactly) -- page 1, q38_draft.py, the install step's check
+ *       that the head is BF16 or FP16; the logits are float32 values
+ *       rounded to BF16 before the argmax and the scatter, as the BF16
+ *       output of the pages' linear is (page 1, get_top_tokens; page 2,
+ *       compute_logits keeps the processor's dtype)
  *
  * Floating point: every float operation below is one IEEE binary32 operation
  * rounded to nearest-even (built with -ffp-contract=off, no fast-math, SSE).
@@ -58,6 +64,48 @@ static float bf16_value(uint16_t bits) {
     float f;
     memcpy(&f, &u, sizeof f);
     return f;
+}
+
+/* An IEEE binary16 number: sign, 5 exponent bits (bias 15), 10 mantissa
+ * bits; exponent 0 is subnormal (m * 2^-24).  Every value is exact in
+ * binary32. */
+static float f16_value(uint16_t bits) {
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 10) & 31;
+    int m = bits & 1023;
+    double mag;
+    if (e == 31)
+        mag = m ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)m, -24);
+    else
+        mag = ldexp(1.0 + m / 1024.0, e - 15);
+    return (float)(sign ? -mag : mag);
+}
+
+float oracle_f16_value(uint16_t bits) { return f16_value(bits); }
+
+/* BF16 bits of a binary32 rounded to nearest, ties to the even code: of
+ * the two BF16 neighbours of x (x with its low 16 bits cleared, and the
+ * next value away from zero) take the closer one; on a tie the one whose
+ * last bit is 0.  Past the largest finite BF16 the upper neighbour is the
+ * infinity code, whose distance is measured from 2^128, as if the exponent
+ * went on (IEEE overflow). */
+uint16_t oracle_bf16_code(float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    uint32_t lo = u & 0xFFFF0000u, hi = lo + 0x10000u;
+    float flo, fhi;
+    memcpy(&flo, &lo, sizeof flo);
+    memcpy(&fhi, &hi, sizeof fhi);
+    double dhi_val = (double)fhi;
+    if ((hi & 0x7F800000u) == 0x7F800000u)
+        dhi_val = copysign(ldexp(1.0, 128), (double)x);
+    double dlo = fabs((double)x - (double)flo);
+    double dhi = fabs(dhi_val - (double)x);
+    if (dlo < dhi) return (uint16_t)(lo >> 16);
+    if (dhi < dlo) return (uint16_t)(hi >> 16);
+    return (uint16_t)(((lo >> 16) & 1) ? (hi >> 16) : (lo >> 16));
 }
 
 /* ------------------------------------------------------------ E4M3 (OCP) */
@@ -154,9 +202,11 @@ int64_t oracle_build_index(const uint8_t* keep, int64_t vocab, int32_t* idx,
  * nibble when k is even and in the high nibble when k is odd;
  * scales[j*hidden/16 + k/16] is the E4M3 byte of block k/16; *gs the global
  * scale.  A value decodes as e2m1(nibble) * e4m3(scale) * gs. */
-int oracle_nvfp4_quantize(const uint16_t* w, int64_t vocab, int64_t hidden,
-                          const int32_t* idx, int64_t n_rows, uint8_t* packed,
-                          uint8_t* scales, float* gs_out) {
+typedef float (*elem_fn)(uint16_t);
+
+static int nvfp4_quantize(const uint16_t* w, elem_fn value, int64_t vocab,
+                          int64_t hidden, const int32_t* idx, int64_t n_rows,
+                          uint8_t* packed, uint8_t* scales, float* gs_out) {
     if (hidden <= 0 || hidden % 16 != 0 || n_rows <= 0) return ORACLE_EINVAL;
     for (int64_t j = 0; j < n_rows; ++j)
         if (idx[j] < 0 || idx[j] >= vocab) return ORACLE_EINVAL;
@@ -168,7 +218,7 @@ int oracle_nvfp4_quantize(const uint16_t* w, int64_t vocab, int64_t hidden,
     for (int64_t j = 0; j < n_rows; ++j) {
         const uint16_t* row = w + (int64_t)idx[j] * hidden;
         for (int64_t k = 0; k < hidden; ++k) {
-            float a = fabsf(bf16_value(row[k]));
+            float a = fabsf(value(row[k]));
             if (a > amax) amax = a;
         }
     }
@@ -185,7 +235,7 @@ int oracle_nvfp4_quantize(const uint16_t* w, int64_t vocab, int64_t hidden,
             /* C3: block amax, then scale = bmax / (6 * gs), E4M3. */
             float bmax = 0.0f;
             for (int i = 0; i < 16; ++i) {
-                float a = fabsf(bf16_value(blk[i]));
+                float a = fabsf(value(blk[i]));
                 if (a > bmax) bmax = a;
             }
             float s = bmax / six_gs;
@@ -195,7 +245,7 @@ int oracle_nvfp4_quantize(const uint16_t* w, int64_t vocab, int64_t hidden,
             float d = s_dec * gs;
             /* C4: element codes. */
             for (int i = 0; i < 16; ++i) {
-                float x = bf16_value(blk[i]);
+                float x = value(blk[i]);
                 uint8_t nib;
                 if (s_dec == 0.0f)
                     nib = (uint8_t)(signbit(x) ? 8 : 0);
@@ -211,6 +261,22 @@ int oracle_nvfp4_quantize(const uint16_t* w, int64_t vocab, int64_t hidden,
         }
     }
     return ORACLE_OK;
+}
+
+int oracle_nvfp4_quantize(const uint16_t* w, int64_t vocab, int64_t hidden,
+                          const int32_t* idx, int64_t n_rows, uint8_t* packed,
+                          uint8_t* scales, float* gs_out) {
+    return nvfp4_quantize(w, bf16_value, vocab, hidden, idx, n_rows, packed,
+                          scales, gs_out);
+}
+
+/* C12: the same recipe on an FP16 head. */
+int oracle_nvfp4_quantize_f16(const uint16_t* w, int64_t vocab,
+                              int64_t hidden, const int32_t* idx,
+                              int64_t n_rows, uint8_t* packed,
+                              uint8_t* scales, float* gs_out) {
+    return nvfp4_quantize(w, f16_value, vocab, hidden, idx, n_rows, packed,
+                          scales, gs_out);
 }
 
 /* ------------------------------------------------------------- C5 logits */
@@ -273,6 +339,31 @@ int oracle_logits_scatter(const double* L, int64_t batch, int64_t n_rows,
         for (int64_t j = 0; j < n_kept; ++j) {
             if (idx[j] < 0 || idx[j] >= vocab) return ORACLE_EINVAL;
             out[b * vocab + idx[j]] = (float)L[b * n_rows + j];
+        }
+    return ORACLE_OK;
+}
+
+/* C12: the logits as the pages' BF16 linear returns them: each float64
+ * logit rounded to binary32 (the accumulator's precision), then to BF16. */
+int oracle_logits_to_bf16(const double* L, int64_t n, uint16_t* out) {
+    if (n <= 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_code((float)L[i]);
+    return ORACLE_OK;
+}
+
+/* C12: the scatter of C7 in BF16: -inf is 0xFF80; the pad rows are left
+ * out. */
+int oracle_logits_scatter_bf16(const uint16_t* Lb, int64_t batch,
+                               int64_t n_rows, int64_t n_kept,
+                               const int32_t* idx, int64_t vocab,
+                               uint16_t* out) {
+    if (batch <= 0 || n_kept <= 0 || n_kept > n_rows) return ORACLE_EINVAL;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t v = 0; v < vocab; ++v) out[b * vocab + v] = 0xFF80u;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t j = 0; j < n_kept; ++j) {
+            if (idx[j] < 0 || idx[j] >= vocab) return ORACLE_EINVAL;
+            out[b * vocab + idx[j]] = Lb[b * n_rows + j];
         }
     return ORACLE_OK;
 }

@@ -417,6 +417,103 @@ def test_w8a8_logits_match_a_float64_matmul():
     assert L1[0, 9] == -2.0 and np.count_nonzero(L1) == 1
 
 
+# ------------------------------------- reference-compatible mode (C12)
+
+def test_f16_decode_all_codes_matches_numpy():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = codes.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_value(c) for c in range(65536)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert oracle.f16_value(0x0001) == 2.0 ** -24
+    assert oracle.f16_value(0x7BFF) == 65504.0
+
+
+def test_nvfp4_quantize_f16_roundtrip_construction():
+    """The exact construction of the BF16 pin, stored as FP16 (every value
+    is exact there too): the FP16 quantizer returns its codes and scales."""
+    rng = np.random.default_rng(14)
+    packed, scales, wt = _roundtrip_construction(rng, 128, 64)
+    w64 = wt.to(torch.float64).numpy()
+    w16 = w64.astype(np.float16)
+    assert np.array_equal(w16.astype(np.float64), w64)
+    p2, s2, gs = oracle.nvfp4_quantize_f16(w16.view(np.uint16),
+                                           np.arange(128, dtype=np.int32))
+    assert gs == np.float32(2.0 ** -8)
+    assert np.array_equal(s2, scales) and np.array_equal(p2, packed)
+
+
+def test_nvfp4_quantize_f16_agrees_with_bf16_on_shared_values():
+    """A head whose values are exact in both FP16 and BF16 quantizes to the
+    same codes, scales and gs from either; an FP16-only mantissa changes
+    codes where the BF16 rounding of the same head would."""
+    rng = np.random.default_rng(15)
+    # magnitudes in [2^-12, 0.1]: FP16 normals, where every BF16 value fits
+    mag = rng.uniform(2.0 ** -12, 0.1, (256, 96))
+    sign = np.where(rng.integers(0, 2, (256, 96)) == 1, -1.0, 1.0)
+    w = torch.from_numpy((mag * sign).astype(np.float32)).to(torch.bfloat16)
+    w64 = w.to(torch.float64).numpy()
+    w16 = w64.astype(np.float16)
+    assert np.array_equal(w16.astype(np.float64), w64)
+    idx = rng.permutation(256)[:128].astype(np.int32)
+    a = oracle.nvfp4_quantize(_bits(w), idx)
+    b = oracle.nvfp4_quantize_f16(w16.view(np.uint16), idx)
+    assert a[2] == b[2] and np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0])
+    x = (rng.standard_normal((128, 96)) * 0.02).astype(np.float16)
+    c = oracle.nvfp4_quantize_f16(x.view(np.uint16), np.arange(128, dtype=np.int32))
+    d = oracle.nvfp4_quantize(_bits(torch.from_numpy(x.astype(np.float32))
+                                    .to(torch.bfloat16)),
+                              np.arange(128, dtype=np.int32))
+    assert not np.array_equal(c[0], d[0])
+
+
+def test_bf16_code_matches_torch():
+    """Round to nearest, ties to even, against torch's float32 -> bfloat16
+    cast: random magnitudes over 2^-126..2^120 of both signs, every exact
+    tie of a range of BF16 pairs, and values just off the ties."""
+    rng = np.random.default_rng(16)
+    x = (rng.standard_normal(4000) * np.exp2(rng.integers(-126, 120, 4000))
+         ).astype(np.float32)
+    top = np.array([3.3895e38, 3.39e38, 3.3961e38, 3.3962e38, 3.4e38],
+                   dtype=np.float32)  # around the largest BF16 and overflow
+    x = np.concatenate([x, top, -top])
+    base = np.arange(0x3F80, 0x3F80 + 256, dtype=np.uint32) << 16
+    ties = (base | 0x8000).view(np.float32)
+    near = np.concatenate([np.nextafter(ties, np.float32(0)),
+                           np.nextafter(ties, np.float32(np.inf))])
+    vals = np.concatenate([x, ties, -ties, near, [0.0, -0.0]]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy()
+    got = np.array([oracle.bf16_code(v) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref.view(np.uint16))
+
+
+def test_logits_to_bf16_rounds_through_float32():
+    """The float64 logit goes to float32 first (the accumulator's
+    precision), then to BF16: 1 + 2^-8 + 2^-30 becomes the tie 1 + 2^-8 in
+    float32 and then 1.0, where a direct rounding would give 1 + 2^-7."""
+    L = np.array([[1 + 2.0 ** -8 + 2.0 ** -30, -(1 + 2.0 ** -8 + 2.0 ** -30),
+                   3.0, -0.0, 1e-40, 3.4e38, -3.39e38, 3.38e38]])
+    got = oracle.logits_to_bf16(L)
+    ref = torch.from_numpy(L).float().to(torch.bfloat16).view(torch.int16)
+    assert np.array_equal(got, ref.numpy().view(np.uint16))
+    assert got[0, 0] == 0x3F80 and got[0, 1] == 0xBF80
+
+
+def test_scatter_bf16_matches_index_copy():
+    rng = np.random.default_rng(17)
+    idx = np.concatenate([np.sort(rng.choice(500, 100, replace=False)),
+                          np.zeros(28, dtype=np.int64)]).astype(np.int32)
+    idx[100:] = idx[0]
+    Lb = oracle.logits_to_bf16(rng.standard_normal((3, 128)))
+    out = oracle.logits_scatter_bf16(Lb, 100, idx, 500)
+    ref = torch.full((3, 500), float("-inf"), dtype=torch.bfloat16)
+    ref.index_copy_(1, torch.from_numpy(idx[:100]).long(),
+                    torch.from_numpy(Lb[:, :100].view(np.int16)).view(torch.bfloat16))
+    assert np.array_equal(out, ref.view(torch.int16).numpy().view(np.uint16))
+    assert ((out == 0xFF80).sum(axis=1) == 400).all()
+
+
 # ------------------------------------------- readings of silent float steps
 
 def test_block_scale_reading_is_bmax_over_six_gs():
