@@ -58,7 +58,9 @@ def metric_name(case) -> str:
     if case.op == "linear":
         return (f"NVFP4 W4A16 linear µs/step and HBM GB/s (% peak), "
                 f"{case.n_rows}x{case.H}, batch {case.B}")
-    what = "GEMV+argmax" if case.op == "top" else "GEMV+logits scatter"
+    what = {"top": "GEMV+argmax", "logits": "GEMV+logits scatter",
+            "top_bf16": "GEMV+argmax over BF16-rounded logits",
+            "logits_bf16": "GEMV+BF16 logits scatter"}[case.op]
     return (f"draft-head µs/step and HBM GB/s (% peak), {case.fmt.upper()} "
             f"{case.n_rows}x{case.H} {what}, batch {case.B}")
 HBM_PEAK_GBS = 8000.0
@@ -81,6 +83,8 @@ def algorithmic_bytes(fmt, n_rows, hidden, batch, op, vocab):
     b += 4 if fmt != "bf16" else 0
     if op == "logits":
         b += n_rows * 4 + batch * vocab * 4
+    elif op == "logits_bf16":
+        b += n_rows * 4 + batch * vocab * 2
     elif op == "linear":
         b += batch * n_rows * 4
     else:
@@ -138,6 +142,8 @@ class Case:
             raise SystemExit(f"workload {config} is a linear; --op does not "
                              f"apply")
         self.op = op or default_op
+        if self.op in ("top_bf16", "logits_bf16") and fmt != "nvfp4":
+            raise SystemExit("the BF16-rounded ops run on the NVFP4 head")
         self.name = config if fmt == w_.formats[0] else f"{config}_{fmt}"
         if self.op != default_op:
             self.name += f"_{self.op}"
@@ -212,6 +218,18 @@ class Case:
                 if rc:
                     raise dh.DraftHeadError("linear", rc)
             return step
+        if self.op == "logits_bf16":
+            stride = B * self.V * 2
+            nk, V = self.n_kept, self.V
+
+            def step(i):
+                hd = heads[i % R]
+                rc = L.draft_head_logits_compat(
+                    hd[0], hd[1], sc, idx_p, n, nk, H, V, h_ptrs[i % nh], B,
+                    out_p + stride * (i % 2), ws_p, ws_n, sp)
+                if rc:
+                    raise dh.DraftHeadError("logits (BF16)", rc)
+            return step
         if self.op == "logits":
             stride = B * self.V * 4
             nk, V = self.n_kept, self.V
@@ -241,7 +259,12 @@ class Case:
                 if rc:
                     raise dh.DraftHeadError(f"logits ({fmt})", rc)
             return step
-        if fmt == "nvfp4":
+        if self.op == "top_bf16":
+            def call(hd, hp, o):
+                return L.draft_head_top_tokens_compat(hd[0], hd[1], sc, idx_p,
+                                                      n, H, hp, B, o, ws_p,
+                                                      ws_n, sp)
+        elif fmt == "nvfp4":
             def call(hd, hp, o):
                 return L.draft_head_top_tokens(hd[0], hd[1], sc, idx_p, n, H,
                                                hp, B, o, ws_p, ws_n, sp)
@@ -293,6 +316,13 @@ class Case:
             return L, oracle.logits_scatter(L, self.n_kept, self.idx, self.V)
         if self.op == "linear":
             return L, L
+        if self.op in ("top_bf16", "logits_bf16"):
+            Lb = oracle.logits_to_bf16(L)
+            if self.op == "logits_bf16":
+                return L, oracle.logits_scatter_bf16(Lb, self.n_kept,
+                                                     self.idx, self.V)
+            rows = np.argmax(oracle.bf16_bits_value(Lb), axis=1)
+            return L, self.idx[rows]
         return L, oracle.argmax_remap(L, self.idx)[1]
 
 
@@ -375,6 +405,25 @@ def check_logits(out, ref):
             "max_abs_err": float(err.max()) if err.size else 0.0}
 
 
+def check_logits_bf16(got, ref, L64, case):
+    """BF16 logits: equal to the oracle's rounding, or (where the float64
+    logit is within the float32 GEMV's error of a rounding boundary) a BF16
+    value between the roundings of L - err and L + err."""
+    import oracle
+    bad = got != ref
+    n_bad = 0
+    if bad.any():
+        err = 1e-5 + 1e-5 * np.abs(L64)
+        lo = oracle.bf16_bits_value(oracle.logits_scatter_bf16(
+            oracle.logits_to_bf16(L64 - err), case.n_kept, case.idx, case.V))
+        hi = oracle.bf16_bits_value(oracle.logits_scatter_bf16(
+            oracle.logits_to_bf16(L64 + err), case.n_kept, case.idx, case.V))
+        v = oracle.bf16_bits_value(got)
+        n_bad = int((bad & ~((v >= lo) & (v <= hi))).sum())
+    return {"checked_values": int(got.size), "mismatches": n_bad,
+            "boundary_values": int(bad.sum()) - n_bad}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -385,7 +434,8 @@ def main():
     ap.add_argument("--format", default=None,
                     choices=["nvfp4", "e4m3", "w8a8", "bf16"],
                     help="head format (default: the workload's first)")
-    ap.add_argument("--op", default=None, choices=["top", "logits"],
+    ap.add_argument("--op", default=None,
+                    choices=["top", "logits", "top_bf16", "logits_bf16"],
                     help="step kind of a head workload (default: logits for "
                          "the batch-8 logits workload, else top tokens); "
                          "the linear workloads always run the linear")
@@ -437,6 +487,8 @@ def main():
     K, W = args.steps, args.warmup
     if case.op == "logits":
         out = torch.empty((2, B, V), dtype=torch.float32, device=dev)
+    elif case.op == "logits_bf16":
+        out = torch.empty((2, B, V), dtype=torch.bfloat16, device=dev)
     elif case.op == "linear":
         out = torch.empty((2, B, case.n_rows), dtype=torch.float32,
                           device=dev)
@@ -444,7 +496,7 @@ def main():
         out = torch.zeros((K + W, B), dtype=torch.int32, device=dev)
     step = case.make_step(h_ptrs, out, stream)
     for i in range(W):
-        step(K + i if case.op == "top" else i)
+        step(K + i if case.op in ("top", "top_bf16") else i)
     torch.cuda.synchronize()
 
     # Timed region: K back-to-back calls between two events recorded on the
@@ -471,7 +523,14 @@ def main():
     result_cpu, parity = None, None
     if not args.no_cpu_baseline:
         cb = cpu_baseline(case, h_cpu, args.cpu_budget)
-        if case.op in ("logits", "linear"):
+        if case.op == "logits_bf16":
+            hi = (K - 1) % n_h
+            L64, ref = (cb["results"][hi] if hi < len(cb["results"])
+                        else case.oracle_step(h_cpu[hi]))
+            got = out[(K - 1) % 2].cpu().view(torch.int16).numpy().view(
+                np.uint16)
+            parity = check_logits_bf16(got, ref, L64, case)
+        elif case.op in ("logits", "linear"):
             # the last timed step used h[(K-1) % n_h] and buffer (K-1) % 2
             hi = (K - 1) % n_h
             ref = (cb["results"][hi] if hi < len(cb["results"])
@@ -481,7 +540,9 @@ def main():
             parity = check_top(out[:K].cpu().numpy(), cb["results"], case,
                                n_h)
         what = {"logits": "logits scatter", "linear": "dense fp32 out",
-                "top": "argmax, remap"}[case.op]
+                "top": "argmax, remap",
+                "top_bf16": "BF16 rounding, argmax, remap",
+                "logits_bf16": "BF16 logits scatter"}[case.op]
         result_cpu = {
             "value": round(case.nbytes / cb["step_s"] / 1e9, 3),
             "unit": "GB/s",
@@ -518,6 +579,8 @@ def main():
             "format": {"nvfp4": "nvfp4-w4a16", "e4m3": "e4m3-w8a16",
                        "w8a8": "e4m3-w8a8", "bf16": "bf16"}[fmt],
             "step": {"top": "top tokens",
+                     "top_bf16": "top tokens over BF16-rounded logits",
+                     "logits_bf16": "BF16 logits to the full vocab",
                      "logits": "fp32 logits to the full vocab",
                      "linear": "NVFP4 W4A16 linear, fp32 out"}[case.op],
             "rotated_head_copies": R, "parallelism": "none (1 GPU)",
@@ -530,7 +593,8 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": load_traffic(case.name, khash),
             "bytes_per_step": case.nbytes,
-            "launches_per_step": ((2 if case.op == "logits" else 1)
+            "launches_per_step": ((2 if case.op in ("logits", "logits_bf16")
+                                   else 1)
                                   + (1 if fmt == "w8a8" else 0)),
         },
         "cpu_baseline": result_cpu,

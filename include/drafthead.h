@@ -115,6 +115,19 @@ int nvfp4_quantize_rows(const void* w_bf16, int64_t vocab, int64_t hidden,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same quantization of an FP16 head (page 1, "q38_draft.py", the
+ * install step accepts a BF16 or an FP16 head).
+ *   w_f16 [device] vocab x hidden IEEE binary16
+ * Every binary16 value is exact in float32; the recipe, the outputs and the
+ * errors are those of nvfp4_quantize_rows.
+ */
+int nvfp4_quantize_rows_f16(const void* w_f16, int64_t vocab, int64_t hidden,
+                            const int32_t* row_ids, int64_t n_rows,
+                            uint8_t* packed, uint8_t* scales,
+                            float* global_scale, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Greedy draft tokens (page 1, get_top_tokens: the argmax over the kept rows
  * of the draft head's output, mapped through dh_idx).
  *   packed, scales, global_scale [device] the NVFP4 head (layout above)
@@ -152,6 +165,35 @@ int draft_head_logits(const uint8_t* packed, const uint8_t* scales,
                       int64_t vocab, const void* h_bf16, int64_t batch,
                       float* out_logits, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * The pages' own numerics, for a caller that must reproduce them (page 1,
+ * get_top_tokens, and page 2, compute_logits, take the argmax and the
+ * scatter of the BF16 output of the drafter's linear).
+ * draft_head_top_tokens_compat: as draft_head_top_tokens, with the argmax
+ *   over c_j = bf16(gs * logit_j) -- the float32 logit times the global
+ *   scale in float32, rounded to nearest-even BF16 -- and the lowest j
+ *   among equal c_j (BF16 values tie often).
+ * draft_head_logits_compat: as draft_head_logits with BF16 output:
+ *   out[b, dh_idx[j]] = bf16(gs * logit_j) for j < n_kept, -inf (0xFF80)
+ *   elsewhere; out_logits_bf16 is batch x vocab BF16, 16-byte aligned.
+ * Errors: as draft_head_top_tokens / draft_head_logits.
+ */
+int draft_head_top_tokens_compat(const uint8_t* packed,
+                                 const uint8_t* scales,
+                                 const float* global_scale,
+                                 const int32_t* dh_idx, int64_t n_rows,
+                                 int64_t hidden, const void* h_bf16,
+                                 int64_t batch, int32_t* out_ids,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+int draft_head_logits_compat(const uint8_t* packed, const uint8_t* scales,
+                             const float* global_scale,
+                             const int32_t* dh_idx, int64_t n_rows,
+                             int64_t n_kept, int64_t hidden, int64_t vocab,
+                             const void* h_bf16, int64_t batch,
+                             void* out_logits_bf16, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * NVFP4 W4A16 linear for the drafter's other projections (page 1,

@@ -61,6 +61,16 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize_rows.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr,
                                           _c_i64, _c_ptr, _c_ptr, _c_ptr,
                                           _c_ptr, _c_size, _c_ptr]
+        L.nvfp4_quantize_rows_f16.restype = ctypes.c_int
+        L.nvfp4_quantize_rows_f16.argtypes = L.nvfp4_quantize_rows.argtypes
+        L.draft_head_top_tokens_compat.restype = ctypes.c_int
+        L.draft_head_top_tokens_compat.argtypes = [
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64,
+            _c_ptr, _c_ptr, _c_size, _c_ptr]
+        L.draft_head_logits_compat.restype = ctypes.c_int
+        L.draft_head_logits_compat.argtypes = [
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64,
+            _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_size, _c_ptr]
         L.draft_head_top_tokens.restype = ctypes.c_int
         L.draft_head_top_tokens.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                             _c_i64, _c_i64, _c_ptr, _c_i64,
@@ -173,8 +183,9 @@ def new_workspace(n_rows: int, batch: int, device="cuda") -> torch.Tensor:
 def nvfp4_quantize_rows(w: torch.Tensor, row_ids: torch.Tensor, *,
                         packed=None, scales=None, global_scale=None,
                         workspace=None, stream=None):
-    """Gather W[row_ids] and quantize to NVFP4 on the GPU.
-    Returns (packed u8 [n,H/2], scales u8 [n,H/16], global_scale f32 [1])."""
+    """Gather W[row_ids] and quantize to NVFP4 on the GPU; w is BF16 or
+    FP16.  Returns (packed u8 [n,H/2], scales u8 [n,H/16], global_scale
+    f32 [1])."""
     V, H = w.shape
     n = row_ids.shape[0]
     dev = w.device
@@ -186,14 +197,16 @@ def nvfp4_quantize_rows(w: torch.Tensor, row_ids: torch.Tensor, *,
         global_scale = torch.empty(1, dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = new_workspace(max(n, 1), 1, dev)
-    rc = lib().nvfp4_quantize_rows(
-        _dev(w, "w", torch.bfloat16), V, H,
+    f16 = w.dtype == torch.float16
+    fn = lib().nvfp4_quantize_rows_f16 if f16 else lib().nvfp4_quantize_rows
+    rc = fn(
+        _dev(w, "w", torch.float16 if f16 else torch.bfloat16), V, H,
         _dev(row_ids, "row_ids", torch.int32), n,
         _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
         _dev(global_scale, "global_scale", torch.float32),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(dev, stream))
-    _check("nvfp4_quantize_rows", rc)
+    _check("nvfp4_quantize_rows_f16" if f16 else "nvfp4_quantize_rows", rc)
     return packed, scales, global_scale
 
 
@@ -241,6 +254,54 @@ def draft_head_logits(packed, scales, global_scale, dh_idx, n_kept: int,
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(dev, stream))
     _check("draft_head_logits", rc)
+    return out
+
+
+# --------------------------------- the pages' own numerics (BF16 logits)
+
+def draft_head_top_tokens_compat(packed, scales, global_scale, dh_idx, h, *,
+                                 out_ids=None, workspace=None, stream=None):
+    """Greedy draft tokens over the logits rounded to BF16 (global scale
+    applied, lowest row on ties), as the pages' BF16 linear feeds the
+    argmax: int32 [B] target ids."""
+    n = packed.shape[0]
+    B, H = h.shape
+    dev = h.device
+    if out_ids is None:
+        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(n, B, dev)
+    rc = lib().draft_head_top_tokens_compat(
+        _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
+        _dev(global_scale, "global_scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, H,
+        _dev(h, "h", torch.bfloat16), B, _dev(out_ids, "out_ids", torch.int32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_top_tokens_compat", rc)
+    return out_ids
+
+
+def draft_head_logits_compat(packed, scales, global_scale, dh_idx,
+                             n_kept: int, vocab: int, h, *, out=None,
+                             workspace=None, stream=None):
+    """BF16 [B, vocab] logits (global scale applied, rounded to nearest
+    even), -inf at ids that were not kept."""
+    n = packed.shape[0]
+    B, H = h.shape
+    dev = h.device
+    if out is None:
+        out = torch.empty((B, vocab), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = new_workspace(n, B, dev)
+    rc = lib().draft_head_logits_compat(
+        _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
+        _dev(global_scale, "global_scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, int(n_kept), H, int(vocab),
+        _dev(h, "h", torch.bfloat16), B, _dev(out, "out", torch.bfloat16),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(dev, stream))
+    _check("draft_head_logits_compat", rc)
     return out
 
 
@@ -448,7 +509,9 @@ def draft_head_logits_bf16(w, dh_idx, n_kept: int, vocab: int, h, *,
 __all__ = [
     "DraftHeadError", "lib", "error_string", "draft_head_build_index",
     "draft_head_workspace_bytes", "new_workspace", "nvfp4_quantize_rows",
-    "draft_head_top_tokens", "draft_head_logits", "nvfp4_linear",
+    "draft_head_top_tokens", "draft_head_logits",
+    "draft_head_top_tokens_compat", "draft_head_logits_compat",
+    "nvfp4_linear",
     "e4m3_quantize_rows_per_tensor", "draft_head_top_tokens_e4m3",
     "draft_head_logits_e4m3", "fp8_quantize_tokens",
     "draft_head_workspace_bytes_w8a8", "new_workspace_w8a8",

@@ -71,7 +71,7 @@ static int top_tokens(int fmt, const void* w, const uint8_t* scales,
                       const float* scale, const int32_t* dh_idx,
                       int64_t n_rows, int64_t hidden, const void* h,
                       int64_t batch, int32_t* out_ids, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      size_t ws_bytes, void* stream, bool bf16 = false) {
   if (!out_ids || !aligned(out_ids, 4)) return DH_EINVAL;
   const int rc = check_head(fmt, w, scales, scale, dh_idx, n_rows, hidden, h,
                             batch, ws, ws_bytes);
@@ -88,6 +88,7 @@ static int top_tokens(int fmt, const void* w, const uint8_t* scales,
   a.batch = batch;
   a.out_ids = out_ids;
   a.ws = static_cast<uint8_t*>(ws);
+  a.bf16_logits = bf16;
   return status(launch_gemv(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -95,7 +96,7 @@ static int logits(int fmt, const void* w, const uint8_t* scales,
                   const float* scale, const int32_t* dh_idx, int64_t n_rows,
                   int64_t n_kept, int64_t hidden, int64_t vocab, const void* h,
                   int64_t batch, float* out, void* ws, size_t ws_bytes,
-                  void* stream) {
+                  void* stream, bool bf16 = false) {
   if (!out || !aligned(out, 16)) return DH_EINVAL;
   if (n_kept < 1 || n_kept > n_rows || vocab < n_kept || vocab > INT32_MAX)
     return DH_EINVAL;
@@ -116,7 +117,37 @@ static int logits(int fmt, const void* w, const uint8_t* scales,
   a.n_kept = n_kept;
   a.vocab = vocab;
   a.ws = static_cast<uint8_t*>(ws);
+  a.bf16_logits = bf16;
   return status(launch_gemv(a, static_cast<hipStream_t>(stream)));
+}
+
+static int check_quant(const void* w, int64_t vocab, int64_t hidden,
+                       const int32_t* ids, int64_t n_rows, const void* out,
+                       uintptr_t out_align, const float* scale,
+                       const void* ws, size_t ws_bytes);
+
+// NVFP4 quantization of a BF16 or FP16 head.
+static int quantize_nvfp4(const void* w, bool f16, int64_t vocab,
+                          int64_t hidden, const int32_t* row_ids,
+                          int64_t n_rows, uint8_t* packed, uint8_t* scales,
+                          float* global_scale, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!scales) return DH_EINVAL;
+  const int rc = check_quant(w, vocab, hidden, row_ids, n_rows, packed, 8,
+                             global_scale, ws, ws_bytes);
+  if (rc != DH_OK) return rc;
+  QuantArgs a;
+  a.w = static_cast<const uint16_t*>(w);
+  a.vocab = vocab;
+  a.hidden = hidden;
+  a.ids = row_ids;
+  a.n_rows = n_rows;
+  a.packed = packed;
+  a.scales = scales;
+  a.global_scale = global_scale;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.f16 = f16;
+  return status(launch_nvfp4_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
 // W8A8 workspace: the GEMV's own workspace, then the tokens' activations
@@ -247,23 +278,19 @@ int nvfp4_quantize_rows(const void* w_bf16, int64_t vocab, int64_t hidden,
                         uint8_t* packed, uint8_t* scales, float* global_scale,
                         void* workspace, size_t workspace_bytes,
                         void* stream) {
-  if (!scales) return DH_EINVAL;
-  const int rc = dh::check_quant(w_bf16, vocab, hidden, row_ids, n_rows,
-                                 packed, 8, global_scale, workspace,
-                                 workspace_bytes);
-  if (rc != DH_OK) return rc;
-  dh::QuantArgs a;
-  a.w = static_cast<const uint16_t*>(w_bf16);
-  a.vocab = vocab;
-  a.hidden = hidden;
-  a.ids = row_ids;
-  a.n_rows = n_rows;
-  a.packed = packed;
-  a.scales = scales;
-  a.global_scale = global_scale;
-  a.ws = static_cast<uint8_t*>(workspace);
-  return dh::status(
-      dh::launch_nvfp4_quantize(a, static_cast<hipStream_t>(stream)));
+  return dh::quantize_nvfp4(w_bf16, false, vocab, hidden, row_ids, n_rows,
+                            packed, scales, global_scale, workspace,
+                            workspace_bytes, stream);
+}
+
+int nvfp4_quantize_rows_f16(const void* w_f16, int64_t vocab, int64_t hidden,
+                            const int32_t* row_ids, int64_t n_rows,
+                            uint8_t* packed, uint8_t* scales,
+                            float* global_scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return dh::quantize_nvfp4(w_f16, true, vocab, hidden, row_ids, n_rows,
+                            packed, scales, global_scale, workspace,
+                            workspace_bytes, stream);
 }
 
 int e4m3_quantize_rows_per_tensor(const void* w_bf16, int64_t vocab,
@@ -306,6 +333,32 @@ int draft_head_logits(const uint8_t* packed, const uint8_t* scales,
   return dh::logits(dh::FMT_NVFP4, packed, scales, global_scale, dh_idx,
                     n_rows, n_kept, hidden, vocab, h_bf16, batch, out_logits,
                     workspace, workspace_bytes, stream);
+}
+
+int draft_head_top_tokens_compat(const uint8_t* packed,
+                                 const uint8_t* scales,
+                                 const float* global_scale,
+                                 const int32_t* dh_idx, int64_t n_rows,
+                                 int64_t hidden, const void* h_bf16,
+                                 int64_t batch, int32_t* out_ids,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return dh::top_tokens(dh::FMT_NVFP4, packed, scales, global_scale, dh_idx,
+                        n_rows, hidden, h_bf16, batch, out_ids, workspace,
+                        workspace_bytes, stream, true);
+}
+
+int draft_head_logits_compat(const uint8_t* packed, const uint8_t* scales,
+                             const float* global_scale,
+                             const int32_t* dh_idx, int64_t n_rows,
+                             int64_t n_kept, int64_t hidden, int64_t vocab,
+                             const void* h_bf16, int64_t batch,
+                             void* out_logits_bf16, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return dh::logits(dh::FMT_NVFP4, packed, scales, global_scale, dh_idx,
+                    n_rows, n_kept, hidden, vocab, h_bf16, batch,
+                    static_cast<float*>(out_logits_bf16), workspace,
+                    workspace_bytes, stream, true);
 }
 
 int nvfp4_linear(const uint8_t* packed, const uint8_t* scales,

@@ -40,6 +40,7 @@ struct QuantArgs {
   uint8_t* scales;
   float* global_scale;
   uint8_t* ws;
+  bool f16 = false;  // w holds binary16 values instead of BF16
 };
 hipError_t launch_nvfp4_quantize(const QuantArgs& a, hipStream_t s);
 
@@ -81,6 +82,10 @@ struct GemvArgs {
   // Logits only: one more factor per batch row (the W8A8 head's token
   // scales), null for none.
   const float* row_scale = nullptr;
+  // The pages' own numerics (NVFP4 only): the top token of the scaled
+  // logits rounded to BF16, or BF16 logits (out_logits then points to
+  // BF16 [batch][vocab]).
+  bool bf16_logits = false;
 };
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
 

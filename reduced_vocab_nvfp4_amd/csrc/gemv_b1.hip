@@ -78,13 +78,16 @@ __device__ __forceinline__ void compute_rows(const Rows<F, C>& r,
   for (int i = 0; i < C; ++i)
     acc = F::chunk_dot(r.p[i], F::SCALED ? r.s[i] : 0u, hreg + i * HD, acc);
   const float v = group_sum<G>(acc);
-  if constexpr (MODE != OUT_TOP) {
+  if constexpr (!is_top(MODE)) {
     if (g == 0 && row < a.n_kept)
-      a.out_logits[out_col<MODE>(a.dh_idx, row)] = v * sc;
-  } else if (v > best_v) {
-    // rows reach a lane in ascending order: strict > keeps the lowest
-    best_v = v;
-    best_r = (int)row;
+      store_logit<MODE>(a.out_logits, out_col<MODE>(a.dh_idx, row), v * sc);
+  } else {
+    const float c = top_value<MODE>(v, sc);
+    if (c > best_v) {
+      // rows reach a lane in ascending order: strict > keeps the lowest
+      best_v = c;
+      best_r = (int)row;
+    }
   }
 }
 
@@ -92,7 +95,7 @@ __device__ __forceinline__ void compute_rows(const Rows<F, C>& r,
 // threads per block.
 template <class F, int G, int C, int MODE, int NB, int NT>
 __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
-  constexpr bool LOGITS = MODE != OUT_TOP;
+  constexpr bool LOGITS = !is_top(MODE);
   constexpr int R = 64 / G;  // rows per wave iteration
   constexpr int NW = NT / 64;
   constexpr int HD = F::EPC / 2;           // h dwords per chunk
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
       hreg[i * HD + 4 * q + 3] = v.w;
     }
   }
-  const float sc = LOGITS ? logit_scale(a, 0) : 1.0f;
+  const float sc = MODE != OUT_TOP ? logit_scale(a, 0) : 1.0f;
   float best_v = -INFINITY;
   int best_r = INT_MAX;
 
@@ -256,6 +259,14 @@ bool pick_fmt(int64_t hidden, int mode, KernelDesc* d) {
     case OUT_SCATTER: return pick<F, OUT_SCATTER>(chunks, d);
     case OUT_DENSE:
       if constexpr (F::kFmt == FMT_NVFP4) return pick<F, OUT_DENSE>(chunks, d);
+      return false;
+    case OUT_TOP_BF16:
+      if constexpr (F::kFmt == FMT_NVFP4)
+        return pick<F, OUT_TOP_BF16>(chunks, d);
+      return false;
+    case OUT_SCATTER_BF16:
+      if constexpr (F::kFmt == FMT_NVFP4)
+        return pick<F, OUT_SCATTER_BF16>(chunks, d);
       return false;
   }
   return false;

@@ -23,8 +23,40 @@ namespace dh {
 // What a GEMV launch writes: the top token per batch row (through the
 // argmax finish), the fp32 logits scattered to the full vocabulary at
 // dh_idx[j] for j < n_kept, or the fp32 output of every row densely,
-// out[b][j] (the plain linear).
-enum OutMode : int { OUT_TOP = 0, OUT_SCATTER = 1, OUT_DENSE = 2 };
+// out[b][j] (the plain linear).  The two BF16 modes are the pages' own
+// numerics (their linear returns BF16): the top token of the logits
+// (tensor scale applied) rounded to BF16, lowest row on ties, and the BF16
+// logits scattered.
+enum OutMode : int {
+  OUT_TOP = 0,
+  OUT_SCATTER = 1,
+  OUT_DENSE = 2,
+  OUT_TOP_BF16 = 3,
+  OUT_SCATTER_BF16 = 4
+};
+
+constexpr bool is_top(int mode) {
+  return mode == OUT_TOP || mode == OUT_TOP_BF16;
+}
+
+// Stores one logit (already scaled) in the mode's output type.
+template <int MODE>
+__device__ __forceinline__ void store_logit(float* out, int64_t off,
+                                            float v) {
+  if constexpr (MODE == OUT_SCATTER_BF16)
+    reinterpret_cast<__bf16*>(out)[off] = (__bf16)v;  // round to nearest even
+  else
+    out[off] = v;
+}
+
+// The value the argmax compares: the unscaled logit (a positive scale does
+// not change the order), or in the BF16 mode the scaled logit rounded to
+// BF16, as the pages' argmax sees it.
+template <int MODE>
+__device__ __forceinline__ float top_value(float v, float sc) {
+  if constexpr (MODE == OUT_TOP_BF16) return (float)(__bf16)(v * sc);
+  return v;
+}
 
 // Output column of row j in the logits modes.
 template <int MODE>

@@ -27,6 +27,21 @@ __global__ __launch_bounds__(FILL_THREADS) void k_fill_neg_inf(float* out,
     out[i] = ninf;
 }
 
+// The same fill for BF16 logits: -inf is 0xFF80, eight to a 16-byte store.
+__global__ __launch_bounds__(FILL_THREADS) void k_fill_neg_inf_bf16(
+    uint16_t* out, int64_t n) {
+  const int64_t n8 = n / 8;
+  uint4* o8 = reinterpret_cast<uint4*>(out);
+  const uint32_t w = 0xFF80FF80u;
+  const int64_t stride = (int64_t)gridDim.x * FILL_THREADS;
+  for (int64_t i = (int64_t)blockIdx.x * FILL_THREADS + threadIdx.x; i < n8;
+       i += stride)
+    o8[i] = make_uint4(w, w, w, w);
+  for (int64_t i = n8 * 8 + (int64_t)blockIdx.x * FILL_THREADS + threadIdx.x;
+       i < n; i += stride)
+    out[i] = 0xFF80u;
+}
+
 // Largest generic slice in {8,4,2,1} that fits the remaining rows and LDS.
 int generic_slice(int64_t remaining, int64_t hidden) {
   for (int bc = 8; bc > 1; bc >>= 1)
@@ -35,8 +50,9 @@ int generic_slice(int64_t remaining, int64_t hidden) {
 }
 
 int out_mode(const GemvArgs& ga) {
-  if (ga.out_logits == nullptr) return OUT_TOP;
-  return ga.dense ? OUT_DENSE : OUT_SCATTER;
+  if (ga.out_logits == nullptr) return ga.bf16_logits ? OUT_TOP_BF16 : OUT_TOP;
+  if (ga.dense) return OUT_DENSE;
+  return ga.bf16_logits ? OUT_SCATTER_BF16 : OUT_SCATTER;
 }
 
 hipError_t plan_slice(const GemvArgs& ga, int64_t remaining,
@@ -73,7 +89,11 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     int64_t blocks = (n / 4 + FILL_THREADS - 1) / FILL_THREADS;
     if (blocks > (int64_t)di.cus * 8) blocks = (int64_t)di.cus * 8;
     if (blocks < 1) blocks = 1;
-    k_fill_neg_inf<<<(int)blocks, FILL_THREADS, 0, s>>>(ga.out_logits, n);
+    if (ga.bf16_logits)
+      k_fill_neg_inf_bf16<<<(int)blocks, FILL_THREADS, 0, s>>>(
+          reinterpret_cast<uint16_t*>(ga.out_logits), n);
+    else
+      k_fill_neg_inf<<<(int)blocks, FILL_THREADS, 0, s>>>(ga.out_logits, n);
   }
   for (int64_t b0 = 0; b0 < ga.batch;) {
     KernelDesc d;
@@ -122,7 +142,12 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     k.out_ids = logits ? nullptr : ga.out_ids + b0;
     // dense: every row is written, out has n_rows columns
     const int64_t cols = ga.dense ? ga.n_rows : ga.vocab;
-    k.out_logits = logits ? ga.out_logits + b0 * cols : nullptr;
+    // the slice's first output row (BF16 logits take two bytes each)
+    k.out_logits =
+        logits ? reinterpret_cast<float*>(
+                     reinterpret_cast<char*>(ga.out_logits) +
+                     b0 * cols * (ga.bf16_logits ? 2 : 4))
+               : nullptr;
     k.n_kept = ga.dense ? ga.n_rows : ga.n_kept;
     k.vocab = cols;
     k.ws = ga.ws;

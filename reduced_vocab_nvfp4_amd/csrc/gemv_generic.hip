@@ -13,7 +13,7 @@ constexpr int THREADS = 256;
 
 template <class F, int B, int MODE>
 __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
-  constexpr bool LOGITS = MODE != OUT_TOP;
+  constexpr bool LOGITS = !is_top(MODE);
   constexpr int NW = THREADS / 64;
   constexpr int HD = F::EPU / 2;  // h dwords per unit
   extern __shared__ uint4 hs4[];
@@ -26,7 +26,7 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
     __syncthreads();
   }
   const uint32_t* hs = reinterpret_cast<const uint32_t*>(hs4);
-  const float sc = LOGITS ? tensor_scale(a) : 1.0f;
+  const float sc = MODE != OUT_TOP ? tensor_scale(a) : 1.0f;
   float best_v[B];
   int best_r[B];
 #pragma unroll
@@ -55,11 +55,15 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
       const float v = group_sum<64>(acc[b]);
       if constexpr (LOGITS) {
         if (lane == 0 && row < a.n_kept)
-          a.out_logits[b * a.vocab + out_col<MODE>(a.dh_idx, row)] =
-              v * (a.row_scale ? sc * a.row_scale[b] : sc);
-      } else if (v > best_v[b]) {
-        best_v[b] = v;
-        best_r[b] = (int)row;
+          store_logit<MODE>(a.out_logits,
+                            b * a.vocab + out_col<MODE>(a.dh_idx, row),
+                            v * (a.row_scale ? sc * a.row_scale[b] : sc));
+      } else {
+        const float c = top_value<MODE>(v, sc);
+        if (c > best_v[b]) {
+          best_v[b] = c;
+          best_r[b] = (int)row;
+        }
       }
     }
   }
@@ -89,6 +93,13 @@ bool pick_fmt(int nb, int64_t hidden, int mode, KernelDesc* d) {
     case OUT_SCATTER: ok = pick<F, OUT_SCATTER>(nb, d); break;
     case OUT_DENSE:
       if constexpr (F::kFmt == FMT_NVFP4) ok = pick<F, OUT_DENSE>(nb, d);
+      break;
+    case OUT_TOP_BF16:
+      if constexpr (F::kFmt == FMT_NVFP4) ok = pick<F, OUT_TOP_BF16>(nb, d);
+      break;
+    case OUT_SCATTER_BF16:
+      if constexpr (F::kFmt == FMT_NVFP4)
+        ok = pick<F, OUT_SCATTER_BF16>(nb, d);
       break;
   }
   if (!ok) return false;

@@ -105,7 +105,7 @@ __device__ __forceinline__ void slot_steps(const Slot<F, RT, SPS>& b, int q,
 
 template <class F, int RT, int SPS, int NB, int MODE, int NT>
 __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
-  constexpr bool LOGITS = MODE != OUT_TOP;
+  constexpr bool LOGITS = !is_top(MODE);
   constexpr int NW = NT / 64;
   constexpr int UR = 16 * RT;  // rows per unit
   extern __shared__ uint4 hs[];
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
                 *reinterpret_cast<const uint16_t*>(sb + soff[t] + 8 * c);
           }
     }
-    if constexpr (MODE == OUT_SCATTER) {
+    if constexpr (MODE == OUT_SCATTER || MODE == OUT_SCATTER_BF16) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) b.ids[t] = a.dh_idx[row0 + 16 * t + n];
     }
@@ -213,7 +213,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   float lsc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    lsc[j] = LOGITS && 4 * q + j < nb ? logit_scale(a, 4 * q + j) : 1.0f;
+    lsc[j] = MODE != OUT_TOP && 4 * q + j < nb ? logit_scale(a, 4 * q + j)
+                                                : 1.0f;
   float best_v[4];
   int best_r[4];
 #pragma unroll
@@ -265,7 +266,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   constexpr int SCALE_LOADS =
       wide_scales<F, SPS>() ? SPS / 2 : (F::SCALED ? SPS : 0);
   constexpr int WEIGHT_LOADS =
-      (NB - 1) * (RT * (SPS + SCALE_LOADS) + (MODE == OUT_SCATTER ? RT : 0));
+      (NB - 1) * (RT * (SPS + SCALE_LOADS) +
+                  (MODE == OUT_SCATTER || MODE == OUT_SCATTER_BF16 ? RT : 0));
   static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(WEIGHT_LOADS)
@@ -295,13 +297,17 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
               if constexpr (LOGITS) {
                 const int m = 4 * q + j;
                 if (m < nb && row < a.n_kept)
-                  a.out_logits[(int64_t)m * a.vocab +
-                               (MODE == OUT_DENSE ? row : b.ids[t])] =
-                      v * lsc[j];
-              } else if (v > best_v[j]) {
-                // a lane's rows ascend: strict > keeps the lowest
-                best_v[j] = v;
-                best_r[j] = (int)row;
+                  store_logit<MODE>(a.out_logits,
+                                    (int64_t)m * a.vocab +
+                                        (MODE == OUT_DENSE ? row : b.ids[t]),
+                                    v * lsc[j]);
+              } else {
+                const float c = top_value<MODE>(v, lsc[j]);
+                if (c > best_v[j]) {
+                  // a lane's rows ascend: strict > keeps the lowest
+                  best_v[j] = c;
+                  best_r[j] = (int)row;
+                }
               }
             }
             acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -393,15 +399,17 @@ KernelDesc desc_for(int64_t steps) {
   return desc<F, 1, L>(steps);
 }
 
-// The dense output mode (the linear) exists for NVFP4 only.
-template <class F, int SPS>
-KernelDesc desc_dense(int64_t steps) {
-  if constexpr (F::kFmt == FMT_NVFP4) return desc<F, SPS, OUT_DENSE>(steps);
-  return KernelDesc{nullptr, 0, 0, 0, false};
+// The dense mode (the linear) and the BF16 modes exist for NVFP4 only; an
+// absent kernel is an empty descriptor.
+template <class F, int L>
+constexpr bool has_mode() {
+  return F::kFmt == FMT_NVFP4 || L == OUT_TOP || L == OUT_SCATTER;
 }
-template <class F>
-KernelDesc desc_dense_for(int64_t steps) {
-  if constexpr (F::kFmt == FMT_NVFP4) return desc_for<F, OUT_DENSE>(steps);
+
+template <class F, int L>
+KernelDesc desc_mode(bool one_step, int64_t steps) {
+  if constexpr (has_mode<F, L>())
+    return one_step ? desc<F, 1, L>(steps) : desc_for<F, L>(steps);
   return KernelDesc{nullptr, 0, 0, 0, false};
 }
 
@@ -413,14 +421,18 @@ bool pick(int64_t hidden, int nb, int mode, int lds_per_block,
   const int64_t steps = hidden / (4 * F::EPC);
   // 16-byte scale pieces need 16-byte aligned scale rows; otherwise one step
   // per slot (the odd slot size loads the scales as 16-bit values)
-  if (F::SCALED && (hidden / 16) % 16 != 0)
-    *d = mode == OUT_TOP       ? desc<F, 1, OUT_TOP>(steps)
-         : mode == OUT_SCATTER ? desc<F, 1, OUT_SCATTER>(steps)
-                               : desc_dense<F, 1>(steps);
-  else
-    *d = mode == OUT_TOP       ? desc_for<F, OUT_TOP>(steps)
-         : mode == OUT_SCATTER ? desc_for<F, OUT_SCATTER>(steps)
-                               : desc_dense_for<F>(steps);
+  const bool one = F::SCALED && (hidden / 16) % 16 != 0;
+  switch (mode) {
+    case OUT_TOP: *d = desc_mode<F, OUT_TOP>(one, steps); break;
+    case OUT_SCATTER: *d = desc_mode<F, OUT_SCATTER>(one, steps); break;
+    case OUT_DENSE: *d = desc_mode<F, OUT_DENSE>(one, steps); break;
+    case OUT_TOP_BF16: *d = desc_mode<F, OUT_TOP_BF16>(one, steps); break;
+    case OUT_SCATTER_BF16:
+      *d = desc_mode<F, OUT_SCATTER_BF16>(one, steps);
+      break;
+    default: return false;
+  }
+  if (!d->fn) return false;
   d->lds_bytes = (size_t)(nb + 1) * (size_t)mfma_lds_row_bytes(hidden);
   if (mode == OUT_DENSE) {
     // a split unit's parts are added through LDS: one f32x4 per lane and
@@ -444,12 +456,8 @@ bool mfma_kernel(int fmt, int64_t hidden, int nb, int mode,
                  int lds_per_block, KernelDesc* out) {
   switch (fmt) {
     case FMT_NVFP4: return pick<Nvfp4>(hidden, nb, mode, lds_per_block, out);
-    case FMT_E4M3:
-      return mode != OUT_DENSE &&
-             pick<E4m3>(hidden, nb, mode, lds_per_block, out);
-    case FMT_BF16:
-      return mode != OUT_DENSE &&
-             pick<Bf16>(hidden, nb, mode, lds_per_block, out);
+    case FMT_E4M3: return pick<E4m3>(hidden, nb, mode, lds_per_block, out);
+    case FMT_BF16: return pick<Bf16>(hidden, nb, mode, lds_per_block, out);
   }
   return false;
 }

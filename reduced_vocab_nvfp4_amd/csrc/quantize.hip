@@ -50,6 +50,16 @@ __device__ __forceinline__ uint32_t abs_bf16_max8(const uint4& v) {
   return a > c ? a : c;
 }
 
+// Value of a 16-bit element: BF16, or (F16) IEEE binary16, both exact in
+// binary32.  For either, the magnitude bits (bits & 0x7FFF) order like the
+// magnitudes.
+template <bool F16>
+__device__ __forceinline__ float elem_f32(uint32_t bits16) {
+  if constexpr (F16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  return bf16_to_f32(bits16);
+}
+
 __device__ __forceinline__ float global_scale_from(uint32_t amax_bits) {
   float amax = __uint_as_float(amax_bits);
   return fmaxf(amax, 1e-12f) / 2688.0f;
@@ -94,6 +104,7 @@ struct Tiles {
       : per_row((hidden / 8 + 63) / 64), count(n_rows * per_row) {}
 };
 
+template <bool F16>
 __global__ __launch_bounds__(QTHREADS) void k_gather_amax(
     const uint16_t* __restrict__ w, int64_t hidden,
     const int32_t* __restrict__ ids, int64_t n_rows,
@@ -135,9 +146,9 @@ __global__ __launch_bounds__(QTHREADS) void k_gather_amax(
   if (threadIdx.x == 0) {
     uint32_t r = wmax[0];
     for (int i = 1; i < QWAVES; ++i) r = r > wmax[i] ? r : wmax[i];
-    // |bf16| bits shifted into place are the binary32 bits of the same
-    // non-negative value, whose unsigned order is the numeric order.
-    if (r) atomicMax(amax_bits, r << 16);
+    // the binary32 bits of the largest magnitude: for non-negative values
+    // their unsigned order is the numeric order
+    if (r) atomicMax(amax_bits, __float_as_uint(elem_f32<F16>(r)));
   }
 }
 
@@ -209,6 +220,7 @@ constexpr uint32_t BF16_2P60 = 0x5D80u;
 // convert; a wave that has a block outside the Markstein range (a NaN,
 // |x| > 2^60 or an extreme divisor) encodes the tile with the division and
 // the midpoint count instead.
+template <bool F16>
 __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
     const uint16_t* __restrict__ w, int64_t hidden,
     const int32_t* __restrict__ ids, int64_t n_rows,
@@ -233,14 +245,16 @@ __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
       const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(
           0, (int)bm, DPP_QUAD_1032, 0xF, 0xF, false);
       bm = bm > other ? bm : other;
-      const float bmax = bf16_to_f32(bm);
+      const float bmax = elem_f32<F16>(bm);
       const float s = bmax / six_gs;
       const uint32_t sc = e4m3_encode_nonneg(s);
       const float s_dec = e4m3_decode_nonneg(sc);
       const float d = s_dec * gs;
       const bool zero = s_dec == 0.0f;
       const float rd = 1.0f / d;
-      const bool fast = zero || (divisor_in_range(d) && bm <= BF16_2P60);
+      // (binary16 magnitudes never reach 2^60)
+      const bool fast =
+          zero || (divisor_in_range(d) && (F16 || bm <= BF16_2P60));
       const uint32_t x[4] = {v.x, v.y, v.z, v.w};
       uint32_t out = 0;
       if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
@@ -251,7 +265,7 @@ __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
           for (int h = 0; h < 2; ++h) {
             const uint32_t bits = (x[(e + h) >> 1] >> (((e + h) & 1) * 16)) &
                                   0xFFFFu;
-            const float ax = bf16_to_f32(bits & 0x7FFFu);
+            const float ax = elem_f32<F16>(bits & 0x7FFFu);
             const float q0 = ax * rd;
             const float r = __builtin_fmaf(-q0, d, ax);
             const float mag = zero ? 0.0f : __builtin_fmaf(r, rd, q0);
@@ -264,7 +278,7 @@ __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t bits = (x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          const float ax = bf16_to_f32(bits & 0x7FFFu);
+          const float ax = elem_f32<F16>(bits & 0x7FFFu);
           const uint32_t mag = zero ? 0u : e2m1_code(ax / d);
           out |= (((bits >> 15) << 3) | mag) << (4 * e);
         }
@@ -440,10 +454,17 @@ hipError_t launch_nvfp4_quantize(const QuantArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   uint32_t* amax = reinterpret_cast<uint32_t*>(a.ws + WS_AMAX);
   const int grid = grid_for(a.n_rows, a.hidden, di.cus);
-  k_gather_amax<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
-                                          amax);
-  k_nvfp4_encode<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
-                                           amax, a.packed, a.scales);
+  if (a.f16) {
+    k_gather_amax<true><<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids,
+                                                  a.n_rows, amax);
+    k_nvfp4_encode<true><<<grid, QTHREADS, 0, s>>>(
+        a.w, a.hidden, a.ids, a.n_rows, amax, a.packed, a.scales);
+  } else {
+    k_gather_amax<false><<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids,
+                                                   a.n_rows, amax);
+    k_nvfp4_encode<false><<<grid, QTHREADS, 0, s>>>(
+        a.w, a.hidden, a.ids, a.n_rows, amax, a.packed, a.scales);
+  }
   k_quant_finish<false><<<1, 64, 0, s>>>(amax, a.global_scale);
   return hipGetLastError();
 }
@@ -461,8 +482,8 @@ hipError_t launch_e4m3_quantize(const QuantE4m3Args& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   uint32_t* amax = reinterpret_cast<uint32_t*>(a.ws + WS_AMAX);
   const int grid = grid_for(a.n_rows, a.hidden, di.cus);
-  k_gather_amax<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
-                                          amax);
+  k_gather_amax<false><<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids,
+                                                 a.n_rows, amax);
   k_e4m3_encode<<<grid, QTHREADS, 0, s>>>(a.w, a.hidden, a.ids, a.n_rows,
                                           amax, a.q);
   k_quant_finish<true><<<1, 64, 0, s>>>(amax, a.scale);

@@ -284,3 +284,47 @@ def test_w8a8_workspace_and_arguments_on_the_host():
     assert lg(nk=n + 1) == dh.DH_EINVAL
     assert lg(V=64) == dh.DH_EINVAL
     assert lg(out=FAKE + 4) == dh.DH_EINVAL
+
+
+def test_compat_calls_and_f16_quantize_reject_bad_arguments_on_the_host():
+    L = dh.lib()
+    n, H, B = 128, 256, 2
+    ws = dh.draft_head_workspace_bytes(n, B)
+    a = dict(p=FAKE, s=FAKE, g=FAKE, idx=FAKE, n=n, H=H, h=FAKE, B=B,
+             out=FAKE, ws=FAKE, wsn=ws)
+
+    def top(**kw):
+        x = {**a, **kw}
+        return L.draft_head_top_tokens_compat(
+            x["p"], x["s"], x["g"], x["idx"], x["n"], x["H"], x["h"], x["B"],
+            x["out"], x["ws"], x["wsn"], None)
+
+    def lg(**kw):
+        x = {**a, **kw}
+        return L.draft_head_logits_compat(
+            x["p"], x["s"], x["g"], x["idx"], x["n"], x.get("nk", n), x["H"],
+            x.get("V", 4096), x["h"], x["B"], x["out"], x["ws"], x["wsn"], None)
+    for f in (top, lg):
+        assert f(p=None) == dh.DH_EINVAL
+        assert f(s=None) == dh.DH_EINVAL
+        assert f(g=None) == dh.DH_EINVAL
+        assert f(out=None) == dh.DH_EINVAL
+        assert f(n=100) == dh.DH_EINVAL
+        assert f(B=0) == dh.DH_EINVAL
+        assert f(ws=None) == dh.DH_EWORKSPACE
+        assert f(wsn=ws - 1) == dh.DH_EWORKSPACE
+    assert lg(nk=n + 1) == dh.DH_EINVAL
+    assert lg(out=FAKE + 2) == dh.DH_EINVAL
+
+    def q16(**kw):
+        x = dict(w=FAKE, V=4096, H=256, ids=FAKE, n=128, p=FAKE, s=FAKE,
+                 g=FAKE, ws=FAKE, wsn=dh.draft_head_workspace_bytes(128, 1))
+        x.update(kw)
+        return L.nvfp4_quantize_rows_f16(x["w"], x["V"], x["H"], x["ids"],
+                                         x["n"], x["p"], x["s"], x["g"],
+                                         x["ws"], x["wsn"], None)
+    assert q16(w=None) == dh.DH_EINVAL
+    assert q16(s=None) == dh.DH_EINVAL
+    assert q16(H=40) == dh.DH_EINVAL
+    assert q16(p=FAKE + 4) == dh.DH_EINVAL
+    assert q16(ws=None) == dh.DH_EWORKSPACE
