@@ -552,6 +552,8 @@ def main():
             "single_thread_us_per_step": (
                 round(cb["single_thread_s"] * 1e6, 1)
                 if cb["single_thread_s"] is not None else None),
+            "quantize_ms": (round(cb["quantize_s"] * 1e3, 1)
+                            if cb["quantize_s"] is not None else None),
             "sample": (f"{cb['steps']} full steps of {case.name} (float64 "
                        f"GEMV over {case.n_rows} rows x {H}, batch {B}, "
                        f"{what}), median; host {os.cpu_count()} visible "
