@@ -214,3 +214,14 @@ def test_compat_ties_take_the_lowest_row():
                .item()) == dst
     assert int(dh.draft_head_top_tokens(p, sc, g, hd.idx_gpu, hg)
                .item()) == src
+
+
+@pytest.mark.parametrize("hid", [48, 272])
+def test_compat_generic_kernel(hid):
+    """Hidden sizes no batch-1 or MFMA shape tiles run the generic kernel,
+    in both BF16 modes, at batch 1, 3 and 9 (slices of 8 and 1)."""
+    from tests.test_gpu_parity import Head
+    hd = Head("tiny", hidden=hid)
+    for B in (1, 3, 9):
+        assert _compat_case(hd, wl.hidden_states(B, hid, 350 + B),
+                            f"generic H={hid} B={B}") == 0

@@ -140,3 +140,28 @@ def test_w8a8_workspace_is_reused_across_calls():
         _logits_ok(out.cpu().numpy(),
                    oracle.logits_scatter(L, hd.n_kept, hd.idx, hd.vocab),
                    f"reuse {i} B={B}")
+
+
+@pytest.mark.parametrize("hid", [48, 272])
+def test_w8a8_generic_kernel(hid):
+    """The W8A8 step on hidden sizes that only the generic kernel tiles."""
+    name = "tiny"
+    w_ = wl.WORKLOADS[name]
+    w = H.head_weight(w_.vocab, hid)
+    idx, n_kept = oracle.build_index(wl.keep_mask(w_))
+    idx_g = torch.from_numpy(idx).to(DEV)
+    q, sc = dh.e4m3_quantize_rows_per_tensor(w.to(DEV), idx_g)
+    oq, os_ = oracle.e4m3_tensor_quantize(wl.bf16_bits(w), idx)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    for B in (1, 3, 9):
+        h = wl.hidden_states(B, hid, 360 + B)
+        qx, sx = oracle.fp8_tokens_quantize(wl.bf16_bits(h))
+        L = oracle.w8a8_logits(oq, os_, qx, sx)
+        ids = dh.draft_head_top_tokens_w8a8(q, sc, idx_g, h.to(DEV))
+        _, want = oracle.argmax_remap(L, idx)
+        assert H.check_top_tokens(ids.cpu().numpy(), L, idx, n_kept, want) == 0
+        out = dh.draft_head_logits_w8a8(q, sc, idx_g, n_kept, w_.vocab,
+                                        h.to(DEV))
+        _logits_ok(out.cpu().numpy(),
+                   oracle.logits_scatter(L, n_kept, idx, w_.vocab),
+                   f"w8a8 generic H={hid} B={B}")
