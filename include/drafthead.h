@@ -276,7 +276,8 @@ int fp8_quantize_tokens(const void* h_bf16, int64_t batch, int64_t hidden,
                         uint8_t* qx, float* sx, void* stream);
 
 /* Workspace bytes for the W8A8 head calls below (0 for an invalid shape):
- * the top-token workspace plus room for the quantized tokens. */
+ * the state of any top-token call (its largest batch) plus scratch for the
+ * quantized tokens, so one workspace can serve these and the other calls. */
 size_t draft_head_workspace_bytes_w8a8(int64_t n_rows, int64_t batch,
                                        int64_t hidden);
 

@@ -150,19 +150,22 @@ static int quantize_nvfp4(const void* w, bool f16, int64_t vocab,
   return status(launch_nvfp4_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
-// W8A8 workspace: the GEMV's own workspace, then the tokens' activations
-// (the BF16 values of their E4M3 codes, [batch][hidden]) and their scales.
-// total == 0 for an invalid shape.
+// W8A8 workspace: the argmax state of any top-token call (the slots of the
+// widest batch, so a workspace shared with other calls never overlaps
+// them), then the tokens' activations (the BF16 values of their E4M3 codes,
+// [batch][hidden]) and their scales, scratch that each call rewrites before
+// reading.  total == 0 for an invalid shape.
 struct W8a8Layout {
   size_t act, sx, total;
 };
 
 static W8a8Layout w8a8_layout(int64_t n_rows, int64_t batch, int64_t hidden) {
   W8a8Layout l{};
-  const size_t base = workspace_bytes(n_rows, batch);
-  if (base == 0 || hidden < 16 || hidden > 16384 || hidden % 16 != 0)
+  if (workspace_bytes(n_rows, batch) == 0 || hidden < 16 || hidden > 16384 ||
+      hidden % 16 != 0)
     return l;
-  l.act = (base + 255) / 256 * 256;
+  const size_t state = workspace_bytes(n_rows, MAX_BATCH);
+  l.act = (state + 255) / 256 * 256;
   l.sx = l.act + ((size_t)batch * (size_t)hidden * 2 + 255) / 256 * 256;
   l.total = l.sx + ((size_t)batch * 4 + 255) / 256 * 256;
   return l;

@@ -70,7 +70,7 @@ __device__ __forceinline__ int64_t out_col(const int32_t* dh_idx,
 struct KArgs {
   const uint8_t* w;       // weight rows (format-specific bytes)
   const uint8_t* scales;  // NVFP4 block scales, else unused
-  const float* scale;     // tensor scale (logits only); null = 1
+  const float* scale;     // tensor scale (logits, BF16 top token); null = 1
   const int32_t* dh_idx;
   int64_t n_rows, hidden;
   const uint16_t* h;  // [nb][hidden] BF16, this slice

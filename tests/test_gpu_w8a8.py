@@ -165,3 +165,28 @@ def test_w8a8_generic_kernel(hid):
         _logits_ok(out.cpu().numpy(),
                    oracle.logits_scatter(L, n_kept, idx, w_.vocab),
                    f"w8a8 generic H={hid} B={B}")
+
+
+def test_w8a8_and_other_calls_share_a_workspace():
+    """A workspace sized for the W8A8 calls at batch 1 also serves the
+    W16 top-token calls of the same head at batch 16, interleaved: the
+    tokens' scratch lies past every call's argmax state."""
+    hd = e4m3_head("tiny")
+    ws = dh.new_workspace_w8a8(hd.n_rows, 1, hd.hidden, DEV)
+    assert ws.numel() >= dh.draft_head_workspace_bytes(hd.n_rows, 16)
+    for i in range(4):
+        h1 = wl.hidden_states(1, hd.hidden, 400 + i)
+        ids = dh.draft_head_top_tokens_w8a8(hd.q, hd.scale, hd.idx_gpu,
+                                            h1.to(DEV), workspace=ws)
+        qx, sx = oracle.fp8_tokens_quantize(wl.bf16_bits(h1))
+        L = oracle.w8a8_logits(hd.o_q, hd.o_scale, qx, sx)
+        _, want = oracle.argmax_remap(L, hd.idx)
+        assert H.check_top_tokens(ids.cpu().numpy(), L, hd.idx, hd.n_kept,
+                                  want) == 0
+        h16 = wl.hidden_states(16, hd.hidden, 410 + i)
+        ids16 = dh.draft_head_top_tokens_e4m3(hd.q, hd.scale, hd.idx_gpu,
+                                              h16.to(DEV), workspace=ws)
+        L16 = hd.oracle_logits(h16)
+        _, want16 = oracle.argmax_remap(L16, hd.idx)
+        assert H.check_top_tokens(ids16.cpu().numpy(), L16, hd.idx,
+                                  hd.n_kept, want16) == 0
