@@ -449,7 +449,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU "
+        print("bench.py runs on one GPU only: the library has no multi-GPU "
               "path (the head is replicated per GPU)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
