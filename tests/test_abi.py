@@ -328,3 +328,21 @@ def test_compat_calls_and_f16_quantize_reject_bad_arguments_on_the_host():
     assert q16(H=40) == dh.DH_EINVAL
     assert q16(p=FAKE + 4) == dh.DH_EINVAL
     assert q16(ws=None) == dh.DH_EWORKSPACE
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No CPU fallback: with the HIP library missing, the first call raises
+    instead of computing anything another way."""
+    import subprocess
+    import sys
+    code = ("import reduced_vocab_nvfp4_amd as dh\n"
+            "dh.LIB_PATH = '/nonexistent/libdrafthead.so'\n"
+            "dh._lib = None\n"
+            "try:\n"
+            "    dh.draft_head_workspace_bytes(64, 1)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root,
+                       capture_output=True, text=True, timeout=300)
+    assert "raised:" in r.stdout and "not built" in r.stdout, r.stdout + r.stderr
