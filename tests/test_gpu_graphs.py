@@ -23,18 +23,16 @@ def say(*a):
 
 
 def _check_replays(run, B, hidden, seed, tag, replays=5):
-    """run(h, out=None, ws=None) -> out tensor; captured once with static
-    h/out/ws, replayed with fresh h against an eager call with its own
-    buffers."""
+    """run(h, out=None, fresh=False) -> out tensor.  Captured once with a
+    static h and output, replayed with fresh h against an eager call
+    (fresh=True: its own workspace and output)."""
     h_static = torch.zeros(B, hidden, dtype=torch.bfloat16, device=DEV)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm-up call outside the capture
-        out = run(h_static)
-        ws_out = (out,)
+        out_static = run(h_static)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    out_static = ws_out[0]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run(h_static, out=out_static)
