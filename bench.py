@@ -300,6 +300,23 @@ class Case:
             self.o_head = bits
         return time.perf_counter() - t0
 
+    def oracle_gemv_rows(self, h, m):
+        """The oracle's GEMV over the first m rows only (the part of a step
+        that scales with the head): times a single-thread sample."""
+        import oracle
+        hb = wl.bf16_bits(h)
+        if self.fmt == "nvfp4":
+            p, sc, g = self.o_head
+            return oracle.nvfp4_logits(p[:m], sc[:m], g, hb)
+        if self.fmt == "e4m3":
+            q, sc = self.o_head
+            return oracle.e4m3_tensor_logits(q[:m], sc, hb)
+        if self.fmt == "w8a8":
+            q, sc = self.o_head
+            return oracle.w8a8_logits(q[:m], sc,
+                                      *oracle.fp8_tokens_quantize(hb))
+        return oracle.bf16_logits(self.o_head, self.idx[:m], hb)
+
     def oracle_step(self, h):
         import oracle
         hb = wl.bf16_bits(h)
@@ -347,20 +364,28 @@ def cpu_baseline(case, h_list, budget_s):
             break
     threads = oracle.num_threads()
     step_s = float(np.median(times))
-    # one step on one thread, when it fits the budget (about threads x the
-    # parallel step)
-    single_s = None
-    if step_s * threads <= budget_s:
-        oracle.set_threads(1)
-        try:
+    # one step on one thread: the full step when it fits the budget (about
+    # threads x the parallel step), else the GEMV over a leading slice of
+    # rows scaled to all of them (the rest of a step is a small part of it)
+    single_s, single_rows = None, None
+    oracle.set_threads(1)
+    try:
+        if step_s * threads <= budget_s:
             t0 = time.perf_counter()
             case.oracle_step(h_list[0])
             single_s = time.perf_counter() - t0
-        finally:
-            oracle.set_threads(threads)
+        else:
+            m = max(64, int(case.n_rows * budget_s / 4 / (step_s * threads)))
+            m = min(m - m % 64, case.n_rows)
+            t0 = time.perf_counter()
+            case.oracle_gemv_rows(h_list[0], m)
+            single_s = (time.perf_counter() - t0) * case.n_rows / m
+            single_rows = m
+    finally:
+        oracle.set_threads(threads)
     return {"step_s": step_s, "steps": len(times), "threads": threads,
-            "single_thread_s": single_s, "quantize_s": t_quant,
-            "results": results}
+            "single_thread_s": single_s, "single_thread_rows": single_rows,
+            "quantize_s": t_quant, "results": results}
 
 
 def cpu_model() -> str:
@@ -552,6 +577,9 @@ def main():
             "single_thread_us_per_step": (
                 round(cb["single_thread_s"] * 1e6, 1)
                 if cb["single_thread_s"] is not None else None),
+            # when set: the single-thread figure is the GEMV over this many
+            # leading rows, scaled to the whole head
+            "single_thread_sampled_rows": cb["single_thread_rows"],
             "quantize_ms": (round(cb["quantize_s"] * 1e3, 1)
                             if cb["quantize_s"] is not None else None),
             "sample": (f"{cb['steps']} full steps of {case.name} (float64 "
