@@ -147,7 +147,10 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
     // global_load_lds_dwordx4: M0 holds the wave's LDS destination.  It is
     // issued as inline assembly so that the compiler's wait-count pass,
     // which does not order LDS reads after these copies correctly, leaves
-    // them alone; the explicit wait below covers them.
+    // them alone; the explicit wait below covers them.  (The compiler warns
+    // that M0 is a reserved register on the clobber list: it keeps no value
+    // in M0 across statements and sets it right before each instruction
+    // that reads it, so declaring the clobber is all that is needed.)
     const uint32_t lds_dst = (uint32_t)(uintptr_t)(
         (__attribute__((address_space(3))) void*)(&hl[wv][64 * j]));
     asm volatile(

@@ -232,7 +232,9 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   // have landed; the barrier then covers every wave's.  (The copies are inline
   // assembly with an explicit wait: the compiler does not order LDS reads
   // after global_load_lds on its own, and a __syncthreads fence would also
-  // wait for the weight loads.)
+  // wait for the weight loads.  The clobber of M0, a register the compiler
+  // reserves and sets right before each instruction that reads it, draws a
+  // warning and is all the compiler needs to know.)
   {
     const char* hb = reinterpret_cast<const char*>(a.h);
     const uint32_t lds_base = (uint32_t)(uintptr_t)(
