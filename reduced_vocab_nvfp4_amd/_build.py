@@ -17,8 +17,9 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # quantizer bit-exactness: every float op rounds on its own
     "-ffp-contract=off",
-    # keep single-lane ticket fetches as issued: the atomic optimizer would
-    # rewrite them and read their result right away
+    # keep the quantizer's one-lane atomicMax as written (no wave-level
+    # rewrite of it by the atomic optimizer); the device pass reads this
+    # option, the host pass reports it unused
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-result",
 ]
