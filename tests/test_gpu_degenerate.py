@@ -133,8 +133,17 @@ def test_zero_hidden_state_e4m3_w8a8_and_bf16_heads(B):
                                     ("flash_next_64k", 4),
                                     ("h98k_b16", 16)])
 def test_one_hot_hidden_states_nvfp4_exact(name, B):
+    """At batch 1, four single rows in turn (the batch-1 kernel); otherwise
+    one batch of B rows."""
     hd = head(name)
-    h = _one_hot_h(B, hd.hidden)
+    h = _one_hot_h(max(B, 4), hd.hidden)
+    hs = [h[b:b + 1] for b in range(4)] if B == 1 else [h]
+    ties = sum((_one_hot_nvfp4_case(hd, x, name) for x in hs), [])
+    assert max(ties) >= 2
+
+
+def _one_hot_nvfp4_case(hd, h, name):
+    B = h.shape[0]
     hg = h.to(DEV)
     L = hd.oracle_logits(h)
     kept = hd.idx_o[:hd.n_kept]
@@ -166,13 +175,13 @@ def test_one_hot_hidden_states_nvfp4_exact(name, B):
     # the linear: every output is one rounded product
     y = dh.nvfp4_linear(hd.packed, hd.scales, hd.gs, hg).cpu().numpy()
     assert np.array_equal(y, L.astype(np.float32))
-    assert max(ties) >= 2 or B == 1
+    return ties
 
 
 @pytest.mark.parametrize("B", [1, 16])
 def test_one_hot_hidden_states_e4m3_exact(B):
     e4 = e4m3_head("h98k_b16")
-    h = _one_hot_h(B, e4.hidden)
+    h = _one_hot_h(max(B, 4), e4.hidden)[3 if B == 1 else 0:][:B]
     hg = h.to(DEV)
     L = e4.oracle_logits(h)
     ids = dh.draft_head_top_tokens_e4m3(e4.q, e4.scale, e4.idx_gpu,
@@ -187,3 +196,4 @@ def test_one_hot_hidden_states_e4m3_exact(B):
     ties = [int((L8[b, :e4.n_kept] == L8[b, :e4.n_kept].max()).sum())
             for b in range(B)]
     say(f"[one-hot] E4M3 h98k B={B}: W8A8 rows at the maximum {ties}")
+    assert max(ties) >= 2
