@@ -154,11 +154,13 @@ __device__ __forceinline__ uint32_t finish_epoch(const KArgs& a) {
 // agent-scope atomic loads until both words carry this call's tag; a slot
 // can only hold that tag once this call's owner wrote it, and the values
 // travel inside the atomics, so relaxed ordering suffices.  Column b is
-// collected the same way by block gridDim.x - 1 - b % gridDim.x.  A collector learns of the last slot about one
-// memory round trip after it lands, where counting arrivals costs a
-// completion wait and an atomic round trip per counter level.  While it
-// polls, a collector also fetches dh_idx of each running best row, so the
-// winner's id is usually in hand when the last slot arrives.
+// collected the same way by block gridDim.x - 1 - b % gridDim.x.  A
+// collector keeps two polling rounds in flight, so it learns of the last
+// slot about half a memory round trip after it lands, where counting
+// arrivals costs a completion wait and an atomic round trip per counter
+// level.  At batch 1 it also fetches dh_idx of its running best row after
+// each round, so the winner's id is in hand when the last slot arrives;
+// otherwise the thread holding the winner fetches it at the end.
 //
 // Termination: only the collectors (at most 16 blocks) wait, and only for
 // slots that the other blocks publish without waiting on anything, so those
@@ -221,33 +223,41 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
   // from different CUs (the uncached polling loads of one CU are served one
   // after another), and the collectors are the blocks dispatched last,
   // which tend to finish last, so most slots are there by their first poll.
-  // Thread t polls the slots of blocks t + k * NT, UNR of them per round,
-  // and re-reads only those still pending.
+  // Thread t polls the slots of blocks t + k * NT, UNR of them per round.
+  // Two rounds are in flight: round k+1 is issued before round k is
+  // checked.  Every load of a round is issued whether or not its slot is
+  // still pending (slot indices past the grid are clamped to the last slot,
+  // and their results ignored), so the number of loads outstanding is the
+  // same on every path and the wait before a check covers only the older
+  // round.
   const int nblk = (int)gridDim.x;
   const int ncol = a.nb < B ? a.nb : B;
-  constexpr int UNR = 8;
+  constexpr int UNR = 4;
   for (int b = nblk - 1 - (int)blockIdx.x; b < ncol; b += nblk) {
     float v = -INFINITY;
     int r = INT_MAX;
-    int id = 0;  // dh_idx[r] once r is a row
+    int id = 0, id_row = -1;  // dh_idx[id_row] (batch 1: after each round)
     for (int i0 = threadIdx.x; i0 < nblk; i0 += NT * UNR) {
       uint32_t pending = 0;
+      const FinishSlot* ps[UNR];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
-        if (i0 + u * NT < nblk) pending |= 1u << u;
-      for (int spin = 0; pending != 0; ++spin) {
-        uint64_t tv[UNR], tr[UNR];
+      for (int u = 0; u < UNR; ++u) {
+        const int i = i0 + u * NT;
+        if (i < nblk) pending |= 1u << u;
+        ps[u] = slot + (int64_t)(i < nblk ? i : nblk - 1) * B + b;
+      }
+      uint64_t v0[UNR], r0[UNR], v1[UNR], r1[UNR];
+      auto issue = [&](uint64_t (&tv)[UNR], uint64_t (&tr)[UNR]) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-          tv[u] = tr[u] = 0;
-          if ((pending >> u) & 1u) {
-            const FinishSlot* s = slot + (int64_t)(i0 + u * NT) * B + b;
-            tv[u] = __hip_atomic_load(&s->tv, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-            tr[u] = __hip_atomic_load(&s->tr, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-          }
+          tv[u] = __hip_atomic_load(&ps[u]->tv, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+          tr[u] = __hip_atomic_load(&ps[u]->tr, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
         }
+      };
+      // takes the slots of a round that carry this call's tag in both words
+      auto check = [&](const uint64_t (&tv)[UNR], const uint64_t (&tr)[UNR]) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
           if (!((pending >> u) & 1u) || (tv[u] >> 32) != tg ||
@@ -259,16 +269,26 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
           if (better(fv, fr, v, r)) {
             v = fv;
             r = fr;
-            // fetched now, so the winner's id is usually in hand by the end
-            if (fr >= 0 && fr < a.n_rows) id = a.dh_idx[fr];
           }
         }
-        if (pending != 0) {
-          if (spin >= FINISH_SPIN_LIMIT) {
-            failed = 1;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
+        // one load per round, also unconditional (row 0 until a row wins);
+        // at batch 1 only: the wider slices measured faster fetching the
+        // winner's id once, at the end
+        if constexpr (B == 1) {
+          id_row = (r >= 0 && r < a.n_rows) ? r : 0;
+          id = a.dh_idx[id_row];
+        }
+      };
+      issue(v0, r0);
+      for (int spin = 0; pending != 0; spin += 2) {
+        issue(v1, r1);
+        check(v0, r0);
+        if (pending == 0) break;
+        issue(v0, r0);
+        check(v1, r1);
+        if (pending != 0 && spin >= FINISH_SPIN_LIMIT) {
+          failed = 1;
+          break;
         }
       }
     }
@@ -291,7 +311,8 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
         fr = cr[w];
       }
     if (fr >= 0 && fr < a.n_rows) {
-      if (r == fr) a.out_ids[b] = failed ? -1 : id;
+      if (r == fr)
+        a.out_ids[b] = failed ? -1 : (id_row == r ? id : a.dh_idx[fr]);
     } else if (threadIdx.x == 0) {
       // no row won: only reachable when every logit is NaN
       a.out_ids[b] = failed ? -1 : a.dh_idx[0];
