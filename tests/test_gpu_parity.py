@@ -340,6 +340,26 @@ def test_top_tokens_generic_path_and_minimal_head():
         H.check_top_tokens(ids, L, idx, n, want)
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_top_tokens_generic_kernel_on_a_wide_grid(B):
+    """hidden 48 on 16 384 rows: the generic kernel's grid is as many blocks
+    as the device holds (more than a collector covers in one pass of four
+    slots per thread), so the argmax collection takes several passes."""
+    rng = np.random.default_rng(43 + B)
+    n, Hd = 16384, 48
+    packed, scales = _synthetic_head(rng, n, Hd)
+    idx = np.sort(rng.permutation(200000)[:n]).astype(np.int32)
+    h = wl.hidden_states(B, Hd, 4300 + B)
+    L = oracle.nvfp4_logits(packed, scales, np.float32(0.5), wl.bf16_bits(h))
+    _, want = oracle.argmax_remap(L, idx)
+    ids = dh.draft_head_top_tokens(
+        torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV),
+        torch.full((1,), 0.5, device=DEV), torch.from_numpy(idx).to(DEV),
+        h.to(DEV)).cpu().numpy()
+    say(f"[generic wide grid] n={n} H={Hd} B={B}")
+    assert H.check_top_tokens(ids, L, idx, n, want) == 0
+
+
 # ---------------------------------------------------------------- logits
 
 def _logits_check(hd, h, tag):
