@@ -44,8 +44,8 @@
  *    may share it whatever their head or batch size, and replaying a
  *    captured call is safe.  Calls that may run concurrently need distinct
  *    workspaces.  A top-token call whose blocks could not all publish
- *    within seconds (only possible if the device starves some of them)
- *    writes -1 for the affected batch rows.
+ *    within a fraction of a second (only possible if the device starves
+ *    some of them) writes -1 for the affected batch rows.
  *  - Every function returns DH_OK (0) or a negative DH_E* code; no C++
  *    exception crosses this interface.  Arguments are checked on the host
  *    before any device work is enqueued.  Ids outside [0, vocab) and

@@ -166,7 +166,8 @@ __device__ __forceinline__ uint32_t finish_epoch(const KArgs& a) {
 // slots that the other blocks publish without waiting on anything, so those
 // blocks run to completion wherever and whenever they are dispatched and
 // every wait ends.  The wait is also bounded: after FINISH_SPIN_LIMIT empty
-// polls (seconds) a collector gives up and writes -1 for its batch row.
+// polling rounds (each waits out a memory round trip, so at least a few
+// tenths of a second) a collector gives up and writes -1 for its batch row.
 constexpr int FINISH_SPIN_LIMIT = 1 << 22;
 
 struct FinishSlot {
