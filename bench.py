@@ -22,8 +22,10 @@ Workloads (reduced_vocab_nvfp4_amd/workloads.py; seeded synthetic inputs):
 The timed region streams from HBM: R copies of the head rotate so that
 R x head bytes exceeds twice the 256 MB Infinity Cache.  Timing: HIP events
 recorded on the launch stream before and after K back-to-back calls
-(preceded by a short GPU sleep so the host enqueues ahead of the device);
-`value` is algorithmic bytes per step / GPU time per step.
+(preceded by a short GPU sleep so the host enqueues ahead of the device),
+repeated (5 times by default); `value` is algorithmic bytes per step / the
+median GPU time per step.  When profiles/ holds a rocprofv3 kernel-trace
+figure taken on the current kernel sources, the line carries it too.
 
 Prints one JSON line.
 """
@@ -111,17 +113,30 @@ def kernel_source_hash(csrc=None):
     return h.hexdigest()[:16]
 
 
-def load_traffic(case, kernel_hash):
-    """HBM traffic per step from committed rocprofv3 counter runs, only if
-    they were taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{case}.json")
+def _profile(kind, case, kernel_hash):
+    """A committed profiles/<kind>_<case>.json, only if it was taken on the
+    current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"{kind}_{case}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_hash:
         return None
-    return t.get("hbm_bytes_per_step")
+    return t
+
+
+def load_traffic(case, kernel_hash):
+    """HBM traffic per step from committed rocprofv3 counter runs."""
+    t = _profile("traffic", case, kernel_hash)
+    return t.get("hbm_bytes_per_step") if t else None
+
+
+def load_kernel_time(case, kernel_hash):
+    """Kernel time per step (µs, summed over the step's kernels) from a
+    committed rocprofv3 --kernel-trace --stats run."""
+    t = _profile("kernel_time", case, kernel_hash)
+    return t.get("kernel_us_per_step") if t else None
 
 
 class Case:
@@ -454,6 +469,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed runs of --steps calls; the median is "
+                         "reported")
     ap.add_argument("--config", default="flash_next_64k",
                     choices=sorted(wl.WORKLOADS))
     ap.add_argument("--format", default=None,
@@ -525,23 +543,29 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K back-to-back calls between two events recorded on the
-    # launch stream (per-step event records would add their own gaps).  A
-    # short device-side sleep first lets the host enqueue ahead of the GPU.
+    # launch stream (per-step event records would add their own gaps),
+    # repeated; the median repeat is reported.  A short device-side sleep
+    # before each repeat lets the host enqueue ahead of the GPU.
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    try:
-        torch.cuda._sleep(int(2e7))
-    except (AttributeError, RuntimeError):
-        pass
-    e0.record(stream)
-    for i in range(K):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    us_step = e0.elapsed_time(e1) * 1000.0 / K
+    reps = max(1, args.repeats)
+    rep_us = []
+    t_wall = 0.0
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t_wall0 = time.perf_counter()
+        try:
+            torch.cuda._sleep(int(2e7))
+        except (AttributeError, RuntimeError):
+            pass
+        e0.record(stream)
+        for i in range(K):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_wall += time.perf_counter() - t_wall0
+        rep_us.append(e0.elapsed_time(e1) * 1000.0 / K)
+    us_step = float(np.median(rep_us))
     gbs = case.nbytes / (us_step * 1e-6) / 1e9
 
     # ---- parity against the oracle, and the CPU leg -----------------------
@@ -589,6 +613,7 @@ def main():
         }
 
     khash = kernel_source_hash()
+    k_us = load_kernel_time(case.name, khash)
     rec = {
         "metric": metric_name(case),
         "value": round(gbs, 2),
@@ -598,6 +623,8 @@ def main():
         "warmup": W,
         "ms_per_step": round(us_step / 1000.0, 6),
         "us_per_step": round(us_step, 3),
+        "repeats": reps,
+        "us_per_step_repeats": [round(x, 3) for x in rep_us],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -623,9 +650,12 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": load_traffic(case.name, khash),
             "bytes_per_step": case.nbytes,
-            "launches_per_step": ((2 if case.op in ("logits", "logits_bf16")
-                                   else 1)
-                                  + (1 if fmt == "w8a8" else 0)),
+            "launches_per_step": 1 + (1 if fmt == "w8a8" else 0),
+            # the committed rocprofv3 kernel-trace time of this step on the
+            # current kernel sources (null when the sources changed since)
+            "rocprof_kernel_us": k_us,
+            "rocprof_frac": (round(case.nbytes / (k_us * 1e-6) / 1e9
+                                   / HBM_PEAK_GBS, 4) if k_us else None),
         },
         "cpu_baseline": result_cpu,
         "parity": parity,

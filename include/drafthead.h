@@ -43,9 +43,21 @@
  *    tagged with it), so the caller must not modify it between calls; calls
  *    may share it whatever their head or batch size, and replaying a
  *    captured call is safe.  Calls that may run concurrently need distinct
- *    workspaces.  A top-token call whose blocks could not all publish
- *    within a fraction of a second (only possible if the device starves
- *    some of them) writes -1 for the affected batch rows.
+ *    workspaces.
+ *  - Give-up: the top-token calls combine per-block results across the
+ *    grid, and a collecting block waits at most a bounded number of polling
+ *    rounds (a fraction of a second or more; exceeded only if the device
+ *    starves some blocks of the call).  A collector that gives up writes -1
+ *    for its batch row and sets the uint16 at byte DH_WS_STATUS_OFFSET of
+ *    the workspace.  The status is sticky: a block of the failed call that
+ *    had not started may still leave a result the next call would take for
+ *    its own, so every later top-token call on that workspace writes -1 for
+ *    every batch row at once, without waiting, until the caller zero-fills
+ *    the workspace again (on the same stream, or after the failed call has
+ *    completed).  The uint16 at DH_WS_SPIN_LIMIT_OFFSET (0 after the
+ *    zero-fill) lowers the bound: n > 0 allows n - 1 empty rounds, so 1
+ *    gives up before the first poll; tests use it to reach this path
+ *    without starving the device.
  *  - Every function returns DH_OK (0) or a negative DH_E* code; no C++
  *    exception crosses this interface.  Arguments are checked on the host
  *    before any device work is enqueued.  Ids outside [0, vocab) and
@@ -67,7 +79,12 @@ extern "C" {
 #define DH_EWORKSPACE (-2) /* workspace pointer null or too small */
 #define DH_EHIP (-3)       /* a HIP runtime call or kernel launch failed */
 
-#define DRAFTHEAD_ABI_VERSION 2
+#define DRAFTHEAD_ABI_VERSION 3
+
+/* Byte offsets of the two uint16 fields of a workspace a caller may read or
+ * write (see "Give-up" above). */
+#define DH_WS_STATUS_OFFSET 4
+#define DH_WS_SPIN_LIMIT_OFFSET 6
 
 int drafthead_abi_version(void);
 
@@ -155,7 +172,12 @@ int draft_head_top_tokens(const uint8_t* packed, const uint8_t* scales,
  * out[b, v] = -inf for every v not among dh_idx[0:n_kept];
  * out[b, dh_idx[j]] = global_scale * logit_j (float32) for j < n_kept (the
  * pad rows are not written).  dh_idx[0:n_kept] must be strictly ascending,
- * as draft_head_build_index makes it.
+ * as draft_head_build_index makes it: the -inf fill is part of the same
+ * pass (one launch per batch slice of up to 16 rows), each kept row writing
+ * the ids from just past the previous kept id up to its own, so a mask
+ * with a long run of dropped ids costs the wave owning that run about
+ * run/64 store rounds.  Ids that are not ascending or not below vocab give
+ * wrong logits but no store outside out_logits.
  * Errors: as draft_head_top_tokens, plus DH_EINVAL for n_kept < 1,
  * n_kept > n_rows, vocab < n_kept.
  */

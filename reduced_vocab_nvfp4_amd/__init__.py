@@ -13,6 +13,7 @@ NVFP4 recipe).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -147,6 +148,16 @@ def _stream(device: torch.device, stream) -> int:
     return int(stream.cuda_stream)
 
 
+def _alloc_stream(stream):
+    """Context for the tensors a call allocates for the caller (outputs, a
+    fresh workspace): on the call's stream, so a workspace's zero-fill is
+    ordered before the kernels that read it, and the caching allocator does
+    not hand its memory to work on another stream while the kernels may
+    still use it."""
+    return contextlib.nullcontext() if stream is None else \
+        torch.cuda.stream(stream)
+
+
 # --------------------------------------------------------------- A1 index
 
 def draft_head_build_index(keep_mask) -> tuple[torch.Tensor, int]:
@@ -170,6 +181,31 @@ def draft_head_workspace_bytes(n_rows: int, batch: int) -> int:
     return int(lib().draft_head_workspace_bytes(int(n_rows), int(batch)))
 
 
+# Workspace fields a caller may read or write (DH_WS_STATUS_OFFSET and
+# DH_WS_SPIN_LIMIT_OFFSET in drafthead.h): two uint16.
+WS_STATUS_OFFSET = 4
+WS_SPIN_LIMIT_OFFSET = 6
+
+
+def workspace_gave_up(workspace: torch.Tensor) -> bool:
+    """True once a collecting block of a top-token call on this workspace
+    gave up waiting (its call wrote -1 ids; every later call on it writes -1
+    until the workspace is zero-filled again).  Reads device memory, so it
+    waits for the work queued on the current stream."""
+    return bool(workspace[WS_STATUS_OFFSET:WS_STATUS_OFFSET + 2]
+                .view(torch.int16).item() != 0)
+
+
+def set_workspace_spin_limit(workspace: torch.Tensor, rounds: int) -> None:
+    """Bound a collecting block's empty polling rounds on this workspace
+    (0 = give up before the first poll); a zero-filled workspace has the
+    library's default bound."""
+    if not 0 <= rounds < 0xFFFF:
+        raise ValueError("rounds must be in [0, 65534]")
+    workspace[WS_SPIN_LIMIT_OFFSET:WS_SPIN_LIMIT_OFFSET + 2].view(
+        torch.int16).fill_(rounds + 1)
+
+
 def new_workspace(n_rows: int, batch: int, device="cuda") -> torch.Tensor:
     """A zero-filled workspace for heads of n_rows rows up to this batch."""
     n = draft_head_workspace_bytes(n_rows, batch)
@@ -189,14 +225,15 @@ def nvfp4_quantize_rows(w: torch.Tensor, row_ids: torch.Tensor, *,
     V, H = w.shape
     n = row_ids.shape[0]
     dev = w.device
-    if packed is None:
-        packed = torch.empty((n, H // 2), dtype=torch.uint8, device=dev)
-    if scales is None:
-        scales = torch.empty((n, H // 16), dtype=torch.uint8, device=dev)
-    if global_scale is None:
-        global_scale = torch.empty(1, dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(max(n, 1), 1, dev)
+    with _alloc_stream(stream):
+        if packed is None:
+            packed = torch.empty((n, H // 2), dtype=torch.uint8, device=dev)
+        if scales is None:
+            scales = torch.empty((n, H // 16), dtype=torch.uint8, device=dev)
+        if global_scale is None:
+            global_scale = torch.empty(1, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(max(n, 1), 1, dev)
     f16 = w.dtype == torch.float16
     fn = lib().nvfp4_quantize_rows_f16 if f16 else lib().nvfp4_quantize_rows
     rc = fn(
@@ -218,10 +255,11 @@ def draft_head_top_tokens(packed, scales, global_scale, dh_idx, h, *,
     n, H2 = packed.shape
     B, H = h.shape
     dev = h.device
-    if out_ids is None:
-        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(n, B, dev)
+    with _alloc_stream(stream):
+        if out_ids is None:
+            out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(n, B, dev)
     rc = lib().draft_head_top_tokens(
         _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
         _dev(global_scale, "global_scale", torch.float32),
@@ -242,10 +280,11 @@ def draft_head_logits(packed, scales, global_scale, dh_idx, n_kept: int,
     n, H2 = packed.shape
     B, H = h.shape
     dev = h.device
-    if out is None:
-        out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(n, B, dev)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(n, B, dev)
     rc = lib().draft_head_logits(
         _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
         _dev(global_scale, "global_scale", torch.float32),
@@ -267,10 +306,11 @@ def draft_head_top_tokens_compat(packed, scales, global_scale, dh_idx, h, *,
     n = packed.shape[0]
     B, H = h.shape
     dev = h.device
-    if out_ids is None:
-        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(n, B, dev)
+    with _alloc_stream(stream):
+        if out_ids is None:
+            out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(n, B, dev)
     rc = lib().draft_head_top_tokens_compat(
         _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
         _dev(global_scale, "global_scale", torch.float32),
@@ -290,10 +330,11 @@ def draft_head_logits_compat(packed, scales, global_scale, dh_idx,
     n = packed.shape[0]
     B, H = h.shape
     dev = h.device
-    if out is None:
-        out = torch.empty((B, vocab), dtype=torch.bfloat16, device=dev)
-    if workspace is None:
-        workspace = new_workspace(n, B, dev)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty((B, vocab), dtype=torch.bfloat16, device=dev)
+        if workspace is None:
+            workspace = new_workspace(n, B, dev)
     rc = lib().draft_head_logits_compat(
         _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
         _dev(global_scale, "global_scale", torch.float32),
@@ -313,8 +354,9 @@ def nvfp4_linear(packed, scales, global_scale, h, *, out=None, stream=None):
     n, H2 = packed.shape
     B, H = h.shape
     dev = h.device
-    if out is None:
-        out = torch.empty((B, n), dtype=torch.float32, device=dev)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty((B, n), dtype=torch.float32, device=dev)
     rc = lib().nvfp4_linear(
         _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
         _dev(global_scale, "global_scale", torch.float32), n, H,
@@ -334,12 +376,13 @@ def e4m3_quantize_rows_per_tensor(w: torch.Tensor, row_ids: torch.Tensor, *,
     V, H = w.shape
     n = row_ids.shape[0]
     dev = w.device
-    if q is None:
-        q = torch.empty((n, H), dtype=torch.uint8, device=dev)
-    if scale is None:
-        scale = torch.empty(1, dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(max(n, 1), 1, dev)
+    with _alloc_stream(stream):
+        if q is None:
+            q = torch.empty((n, H), dtype=torch.uint8, device=dev)
+        if scale is None:
+            scale = torch.empty(1, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(max(n, 1), 1, dev)
     rc = lib().e4m3_quantize_rows_per_tensor(
         _dev(w, "w", torch.bfloat16), V, H,
         _dev(row_ids, "row_ids", torch.int32), n, _dev(q, "q", torch.uint8),
@@ -356,10 +399,11 @@ def draft_head_top_tokens_e4m3(q, scale, dh_idx, h, *, out_ids=None,
     n, H = q.shape
     B = h.shape[0]
     dev = h.device
-    if out_ids is None:
-        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(n, B, dev)
+    with _alloc_stream(stream):
+        if out_ids is None:
+            out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(n, B, dev)
     rc = lib().draft_head_top_tokens_e4m3(
         _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
         _dev(dh_idx, "dh_idx", torch.int32), n, H,
@@ -376,10 +420,11 @@ def draft_head_logits_e4m3(q, scale, dh_idx, n_kept: int, vocab: int, h, *,
     n, H = q.shape
     B = h.shape[0]
     dev = h.device
-    if out is None:
-        out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(n, B, dev)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(n, B, dev)
     rc = lib().draft_head_logits_e4m3(
         _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
         _dev(dh_idx, "dh_idx", torch.int32), n, int(n_kept), H, int(vocab),
@@ -397,10 +442,11 @@ def fp8_quantize_tokens(h, *, qx=None, sx=None, stream=None):
     (qx uint8 [B, H] e4m3fn codes, sx float32 [B] scales)."""
     B, H = h.shape
     dev = h.device
-    if qx is None:
-        qx = torch.empty((B, H), dtype=torch.uint8, device=dev)
-    if sx is None:
-        sx = torch.empty(B, dtype=torch.float32, device=dev)
+    with _alloc_stream(stream):
+        if qx is None:
+            qx = torch.empty((B, H), dtype=torch.uint8, device=dev)
+        if sx is None:
+            sx = torch.empty(B, dtype=torch.float32, device=dev)
     rc = lib().fp8_quantize_tokens(
         _dev(h, "h", torch.bfloat16), B, H, _dev(qx, "qx", torch.uint8),
         _dev(sx, "sx", torch.float32), _stream(dev, stream))
@@ -429,10 +475,11 @@ def draft_head_top_tokens_w8a8(q, scale, dh_idx, h, *, out_ids=None,
     n, H = q.shape
     B = h.shape[0]
     dev = h.device
-    if out_ids is None:
-        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
-    if workspace is None:
-        workspace = new_workspace_w8a8(n, B, H, dev)
+    with _alloc_stream(stream):
+        if out_ids is None:
+            out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = new_workspace_w8a8(n, B, H, dev)
     rc = lib().draft_head_top_tokens_w8a8(
         _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
         _dev(dh_idx, "dh_idx", torch.int32), n, H,
@@ -450,10 +497,11 @@ def draft_head_logits_w8a8(q, scale, dh_idx, n_kept: int, vocab: int, h, *,
     n, H = q.shape
     B = h.shape[0]
     dev = h.device
-    if out is None:
-        out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = new_workspace_w8a8(n, B, H, dev)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = new_workspace_w8a8(n, B, H, dev)
     rc = lib().draft_head_logits_w8a8(
         _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
         _dev(dh_idx, "dh_idx", torch.int32), n, int(n_kept), H, int(vocab),
@@ -472,10 +520,11 @@ def draft_head_top_tokens_bf16(w, dh_idx, h, *, out_ids=None, workspace=None,
     n, H = w.shape
     B = h.shape[0]
     dev = h.device
-    if out_ids is None:
-        out_ids = torch.empty(B, dtype=torch.int32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(n, B, dev)
+    with _alloc_stream(stream):
+        if out_ids is None:
+            out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(n, B, dev)
     rc = lib().draft_head_top_tokens_bf16(
         _dev(w, "w", torch.bfloat16), _dev(dh_idx, "dh_idx", torch.int32), n,
         H, _dev(h, "h", torch.bfloat16), B,
@@ -492,10 +541,11 @@ def draft_head_logits_bf16(w, dh_idx, n_kept: int, vocab: int, h, *,
     n, H = w.shape
     B = h.shape[0]
     dev = h.device
-    if out is None:
-        out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = new_workspace(n, B, dev)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = new_workspace(n, B, dev)
     rc = lib().draft_head_logits_bf16(
         _dev(w, "w", torch.bfloat16), _dev(dh_idx, "dh_idx", torch.int32), n,
         int(n_kept), H, int(vocab), _dev(h, "h", torch.bfloat16), B,
@@ -508,7 +558,8 @@ def draft_head_logits_bf16(w, dh_idx, n_kept: int, vocab: int, h, *,
 
 __all__ = [
     "DraftHeadError", "lib", "error_string", "draft_head_build_index",
-    "draft_head_workspace_bytes", "new_workspace", "nvfp4_quantize_rows",
+    "draft_head_workspace_bytes", "new_workspace", "workspace_gave_up",
+    "set_workspace_spin_limit", "nvfp4_quantize_rows",
     "draft_head_top_tokens", "draft_head_logits",
     "draft_head_top_tokens_compat", "draft_head_logits_compat",
     "nvfp4_linear",

@@ -4,6 +4,8 @@
 // declarations in include/drafthead.h.
 #include "drafthead.h"
 
+#include <mutex>
+
 #include "dh_internal.h"
 #include "formats.h"
 
@@ -21,24 +23,30 @@ size_t workspace_bytes(int64_t n_rows, int64_t batch) {
   return WS_SLOTS + (size_t)MAX_GRID * (size_t)slots * 16;
 }
 
+// Queried once per device under a lock, so two host threads making their
+// first call at the same time do not race on the cache.
 hipError_t device_info(DeviceInfo* out) {
-  static DeviceInfo cache[64];
-  static bool have[64];
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static DeviceInfo cache[MAX_DEV];
+  static bool have[MAX_DEV];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && have[dev]) {
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < MAX_DEV && have[dev]) {
     *out = cache[dev];
     return hipSuccess;
   }
   DeviceInfo d{};
+  d.dev = dev;
   e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&d.lds_per_block,
                             hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess) return e;
   if (d.cus < 1) d.cus = 1;
-  if (dev >= 0 && dev < 64) {
+  if (dev >= 0 && dev < MAX_DEV) {
     cache[dev] = d;
     have[dev] = true;
   }

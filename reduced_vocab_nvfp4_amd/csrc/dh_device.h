@@ -54,6 +54,31 @@ __device__ __forceinline__ uint32_t e2m1_encode_mag(float a) {
          (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
 }
 
+// ------------------------------------------------------------ LDS copies
+
+// global_load_lds_dwordx4: the 16 bytes at src of each lane land in LDS at
+// lds_base + 16 * lane (lds_base wave-uniform).  The LDS address travels in
+// M0, which the compiler loads itself for the asm's "{m0}" input operand.
+// This is inline assembly rather than __builtin_amdgcn_global_load_lds
+// because with the builtin the compiler waits for every outstanding vector
+// load (vmcnt(0)) before the first LDS read that follows, which would also
+// wait for the weight loads issued after the copy.  The compiler does not
+// know that the copy writes LDS: the caller waits for it with an explicit
+// s_waitcnt before reading the destination (vector memory loads retire in
+// issue order).
+__device__ __forceinline__ void lds_copy_x4(const void* src,
+                                            uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(lds_base)
+               : "memory");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
 // ------------------------------------------------------------ reductions
 
 // DPP control words (GCN/CDNA encoding).

@@ -11,10 +11,20 @@ namespace dh {
 // Workspace layout (bytes).  The caller zero-fills it once; after that it
 // carries state from call to call and must not be modified between calls.
 //   WS_EPOCH   uint32 call counter of the argmax finish (tags its slots)
+//   WS_STATUS  uint16, nonzero once a collector of the argmax finish gave
+//              up waiting; sticky: every later top-token call on this
+//              workspace writes -1 until the caller zero-fills it again
+//              (DH_WS_STATUS_OFFSET in drafthead.h)
+//   WS_SPIN    uint16 bound on a collector's empty polling rounds: 0 = the
+//              default FINISH_SPIN_LIMIT, n > 0 = n - 1 rounds, so 1 gives
+//              up before the first poll (DH_WS_SPIN_LIMIT_OFFSET)
+//   (the three share the 64-bit word at 0, which every block loads once)
 //   WS_AMAX    amax bits of the quantizers, returned to zero by each call
 //   WS_SLOTS   16-byte tagged (value, row) slots, one per block per batch
 //              row of a slice (at most MAX_SLICE)
 constexpr size_t WS_EPOCH = 0;
+constexpr size_t WS_STATUS = 4;
+constexpr size_t WS_SPIN = 6;
 constexpr size_t WS_AMAX = 64;
 constexpr size_t WS_SLOTS = 256;
 constexpr int MAX_GRID = 4096;  // upper bound of any argmax grid
@@ -26,6 +36,7 @@ size_t workspace_bytes(int64_t n_rows, int64_t batch);
 
 // Properties of the current device, queried once per device.
 struct DeviceInfo {
+  int dev;
   int cus;
   int lds_per_block;
 };

@@ -33,6 +33,7 @@ template <class F, int C>
 struct Rows {
   uint4 p[C];
   uint32_t s[C];
+  int32_t id;  // scatter modes: dh_idx of the group's rows (see load_rows)
 };
 
 // Loads the C chunks (and their scales) of one row group for this lane.
@@ -40,7 +41,7 @@ struct Rows {
 // the lane's first chunk within the group (loop-invariant): the address is a
 // scalar base plus a fixed per-lane offset, so no per-iteration address
 // registers are written while earlier loads are still outstanding.
-template <class F, int G, int C>
+template <class F, int G, int C, int MODE>
 __device__ __forceinline__ void load_rows(Rows<F, C>& r, const KArgs& a,
                                           int64_t row0, uint32_t lane_chunk) {
   constexpr int64_t CPR = (int64_t)G * C;  // chunks per row
@@ -64,6 +65,49 @@ __device__ __forceinline__ void load_rows(Rows<F, C>& r, const KArgs& a,
       r.s[i] =
           *reinterpret_cast<const uint16_t*>(sb + 2u * (lane_chunk + G * i));
   }
+  if constexpr (is_scatter(MODE)) {
+    // lane l < R + 1 loads dh_idx[row0 - 1 + l] (the kept id before the
+    // group, then the group's R ids); the other lanes repeat lane R's
+    constexpr int R = 64 / G;
+    const int l = (int)(threadIdx.x & 63);
+    const int64_t j = row0 - 1 + (l < R ? l : R);
+    r.id = a.dh_idx[j < 0 ? 0 : j];
+  }
+}
+
+// Logits of one row group (scatter modes): the wave writes the id range its
+// kept rows own (owned_ids), the group's logits at their ids and -inf
+// between them.  Called by the whole wave; row0 is wave-uniform and every
+// lane of group i holds row row0 + i's sum v.
+template <int G, int MODE>
+__device__ __forceinline__ void scatter_group(const KArgs& a, int64_t row0,
+                                              int32_t id, float v, float sc) {
+  constexpr int R = 64 / G;
+  if (row0 >= a.n_kept) return;  // pad rows only
+  const int64_t left = a.n_kept - row0;
+  const int nk = left < R ? (int)left : R;
+  int32_t ids[R];
+  float vals[R];
+  int32_t last_id = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    ids[i] = __builtin_amdgcn_readlane(id, i + 1);
+    vals[i] = __int_as_float(
+                  __builtin_amdgcn_readlane(__float_as_int(v), i * G)) *
+              sc;
+    if (i < nk) last_id = ids[i];
+  }
+  const IdRange rg = owned_ids(row0, nk, __builtin_amdgcn_readlane(id, 0),
+                               last_id, a.n_kept, a.vocab);
+  const int lane = (int)(threadIdx.x & 63);
+  for (int64_t p0 = rg.lo; p0 < rg.hi; p0 += 64) {
+    const int64_t p = p0 + lane;
+    float out = not_kept_value<MODE>();
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (i < nk && p == ids[i]) out = vals[i];
+    if (p < rg.hi) store_logit<MODE>(a.out_logits, p, out);
+  }
 }
 
 template <class F, int G, int C, int MODE>
@@ -78,9 +122,11 @@ __device__ __forceinline__ void compute_rows(const Rows<F, C>& r,
   for (int i = 0; i < C; ++i)
     acc = F::chunk_dot(r.p[i], F::SCALED ? r.s[i] : 0u, hreg + i * HD, acc);
   const float v = group_sum<G>(acc);
-  if constexpr (!is_top(MODE)) {
-    if (g == 0 && row < a.n_kept)
-      store_logit<MODE>(a.out_logits, out_col<MODE>(a.dh_idx, row), v * sc);
+  if constexpr (is_scatter(MODE)) {
+    scatter_group<G, MODE>(a, row - (int64_t)(threadIdx.x & 63) / G, r.id, v,
+                           sc);
+  } else if constexpr (MODE == OUT_DENSE) {
+    if (g == 0 && row < a.n_kept) store_logit<MODE>(a.out_logits, row, v * sc);
   } else {
     const float c = top_value<MODE>(v, sc);
     if (c > best_v) {
@@ -106,7 +152,7 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane / G, g = lane % G;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t epoch = LOGITS ? 0u : finish_epoch(a);
+  const FinishState st = LOGITS ? FinishState{} : finish_state(a);
 
   // Row groups are dealt to the grid's waves round-robin (grid stride):
   // wave w of the grid takes groups w, w + TW, w + 2 TW, ...  The per-wave
@@ -144,33 +190,20 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
     // into the slack of the slice
     const int src = (HU4 % 64 == 0 || 64 * j + lane < HU4) ? 64 * j + lane
                                                             : HU4 - 1;
-    // global_load_lds_dwordx4: M0 holds the wave's LDS destination.  It is
-    // issued as inline assembly so that the compiler's wait-count pass,
-    // which does not order LDS reads after these copies correctly, leaves
-    // them alone; the explicit wait below covers them.  (The compiler warns
-    // that M0 is a reserved register on the clobber list: it keeps no value
-    // in M0 across statements and sets it right before each instruction
-    // that reads it, so declaring the clobber is all that is needed.)
-    const uint32_t lds_dst = (uint32_t)(uintptr_t)(
-        (__attribute__((address_space(3))) void*)(&hl[wv][64 * j]));
-    asm volatile(
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %0, off"
-        :
-        : "v"(h4 + src), "s"(lds_dst)
-        : "memory", "m0");
+    lds_copy_x4(h4 + src, lds_addr(&hl[wv][64 * j]));
   }
   __builtin_amdgcn_sched_barrier(0);
   Rows<F, C> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB - 1; ++k)
-    load_rows<F, G, C>(buf[k], a, row0_of(k), lane_chunk);
+    load_rows<F, G, C, MODE>(buf[k], a, row0_of(k), lane_chunk);
   // Memory loads retire in issue order, so once no more than the weight
   // loads just issued are outstanding, the h copies have landed in LDS.
   // (The wait is explicit: the compiler does not order LDS reads after
   // global_load_lds on its own.)  The "memory" clobber keeps the LDS reads
   // below it.
-  constexpr int WEIGHT_LOADS = (NB - 1) * (F::SCALED ? 2 : 1) * C;
+  constexpr int WEIGHT_LOADS =
+      (NB - 1) * ((F::SCALED ? 2 : 1) * C + (is_scatter(MODE) ? 1 : 0));
   static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WEIGHT_LOADS) : "memory");
@@ -195,8 +228,8 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
     for (int it = 0; it < n_pad; it += NB) {
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
-        load_rows<F, G, C>(buf[(k + NB - 1) % NB], a, row0_of(it + k + NB - 1),
-                           lane_chunk);
+        load_rows<F, G, C, MODE>(buf[(k + NB - 1) % NB], a,
+                                 row0_of(it + k + NB - 1), lane_chunk);
         __builtin_amdgcn_sched_barrier(0);
         if (it + k < n_it)  // wave-uniform: padded iterations only load
           compute_rows<F, G, C, MODE>(buf[k], a, row0_of(it + k) + grp, g,
@@ -209,7 +242,7 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   if constexpr (!LOGITS) {
     float bv[1] = {best_v};
     int br[1] = {best_r};
-    argmax_finish<1, NT>(bv, br, a, epoch);
+    argmax_finish<1, NT>(bv, br, a, st);
   }
 }
 

@@ -66,6 +66,38 @@ __device__ __forceinline__ int64_t out_col(const int32_t* dh_idx,
   return dh_idx[row];
 }
 
+constexpr bool is_scatter(int mode) {
+  return mode == OUT_SCATTER || mode == OUT_SCATTER_BF16;
+}
+
+// The value the scatter writes at ids that were not kept.
+template <int MODE>
+__device__ __forceinline__ float not_kept_value() {
+  return -INFINITY;  // 0xFF800000, or 0xFF80 once rounded to BF16
+}
+
+// The id range of the logits that kept rows [r0, r0 + nk) own, nk >= 1,
+// r0 + nk <= n_kept: from just past the previous kept id (0 for row 0) up to
+// their last id, or to the end of the vocabulary for the group holding the
+// last kept row.  The ranges of consecutive groups tile [0, vocab), so
+// every logit is written exactly once, by the wave that owns the kept ids
+// it holds or lies between: the -inf fill needs no launch of its own.  The
+// bounds are clamped to [0, vocab), so ids outside the contract (out of
+// range, not ascending) give wrong logits but never a store out of bounds.
+struct IdRange {
+  int64_t lo, hi;
+};
+__device__ __forceinline__ IdRange owned_ids(int64_t r0, int nk,
+                                             int32_t prev_id,
+                                             int32_t last_id,
+                                             int64_t n_kept, int64_t vocab) {
+  int64_t lo = r0 == 0 ? 0 : (int64_t)prev_id + 1;
+  int64_t hi = r0 + nk == n_kept ? vocab : (int64_t)last_id + 1;
+  if (lo < 0) lo = 0;
+  if (hi > vocab) hi = vocab;
+  return IdRange{lo, hi};
+}
+
 // One launch = one batch slice of at most 16 rows.
 struct KArgs {
   const uint8_t* w;       // weight rows (format-specific bytes)
@@ -124,7 +156,8 @@ __device__ __forceinline__ float logit_scale(const KArgs& a, int m) {
   return a.row_scale ? s * a.row_scale[m] : s;
 }
 
-// Call counter of the argmax slots.  The workspace keeps it; a call's
+// State of the argmax finish kept in the workspace: the call counter of the
+// slots, the sticky give-up status and the polling-round bound.  A call's
 // blocks tag their slots with counter + 1 (0 is skipped: a zero-filled slot
 // is never valid) and the collecting block stores the tag back as the new
 // counter once it has read every slot.  The previous call's store is
@@ -132,18 +165,26 @@ __device__ __forceinline__ float logit_scale(const KArgs& a, int m) {
 // counter after the collector writes it (every block reads it before it
 // publishes), so a plain load suffices.  Every wave issues it at the
 // kernel's start, unconditionally, and only the argmax finish uses the
-// value: its latency then hides behind the kernel's own work.  (It is an
-// atomic load only to keep the compiler from turning it into a scalar load,
-// whose wait would coincide with the first LDS wait.)
-__device__ __forceinline__ uint32_t finish_epoch(const KArgs& a) {
-  return __hip_atomic_load(reinterpret_cast<uint32_t*>(a.ws + WS_EPOCH),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// values: their latency then hides behind the kernel's own work.  (They are
+// atomic loads only to keep the compiler from turning them into scalar
+// loads, whose wait would coincide with the first LDS wait.)
+struct FinishState {
+  uint64_t word;  // WS_EPOCH .. WS_SPIN
+  __device__ uint32_t epoch() const { return (uint32_t)word; }
+  __device__ uint32_t status() const { return (uint32_t)(word >> 32) & 0xFFFFu; }
+  __device__ uint32_t spin() const { return (uint32_t)(word >> 48); }
+};
+
+__device__ __forceinline__ FinishState finish_state(const KArgs& a) {
+  return FinishState{
+      __hip_atomic_load(reinterpret_cast<uint64_t*>(a.ws + WS_EPOCH),
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)};
 }
 
 // Block-level (value,row) reduction, the partial write and the collection
 // of the partials.  best_v/best_r are this lane's candidates for the B batch
 // columns of the slice (B = the slice's compile-time capacity; only the
-// first a.nb are written out).  epoch = finish_epoch(a), loaded at the
+// first a.nb are written out).  st = finish_state(a), loaded at the
 // kernel's start (only thread 0's value is used).
 //
 // Cross-block protocol.  Every block publishes its (value, row) per batch
@@ -167,7 +208,13 @@ __device__ __forceinline__ uint32_t finish_epoch(const KArgs& a) {
 // blocks run to completion wherever and whenever they are dispatched and
 // every wait ends.  The wait is also bounded: after FINISH_SPIN_LIMIT empty
 // polling rounds (each waits out a memory round trip, so at least a few
-// tenths of a second) a collector gives up and writes -1 for its batch row.
+// tenths of a second; the workspace's WS_SPIN word can lower the bound) a
+// collector gives up, writes -1 for its batch row and sets the workspace's
+// status word.  A block that had not started by then may still publish a
+// slot with a tag the next call would also use, so a workspace whose status
+// is set is never polled again: every later call's collectors write -1 at
+// once, until the caller zero-fills the workspace (after the failed call
+// has completed, so no block of it still runs).
 constexpr int FINISH_SPIN_LIMIT = 1 << 22;
 
 struct FinishSlot {
@@ -186,7 +233,7 @@ struct WaveBest {
 template <int B, int NT>
 __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
                                                   const KArgs& a,
-                                                  uint32_t epoch) {
+                                                  const FinishState& st) {
   static_assert(B >= 1 && B <= 64 && NT % 64 == 0, "columns within a wave");
   constexpr int NW = NT / 64;
   const float(&sv)[NW][B] = w.v;
@@ -195,11 +242,22 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
   __shared__ int cr[NW];
   __shared__ int failed;
   __shared__ uint32_t block_tag;
+  __shared__ int spin_limit;  // -1: give up without polling
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   FinishSlot* slot = reinterpret_cast<FinishSlot*>(a.ws + WS_SLOTS);
   if (threadIdx.x == 0) {
+    // The state word was loaded at the kernel's start; the empty asm keeps
+    // the compiler from moving its first use (a move to scalar registers,
+    // which waits for the load) up there.
+    FinishState fs = st;
+    asm volatile("" : "+v"(fs.word));
     failed = 0;
-    block_tag = epoch + 1 == 0 ? 1u : epoch + 1;
+    block_tag = fs.epoch() + 1 == 0 ? 1u : fs.epoch() + 1;
+    // rounds a collector may poll; a workspace whose status is set is never
+    // polled again (see above), and a bound of 0 rounds gives up at once
+    const uint32_t sp = fs.spin();
+    const int lim = sp == 0 ? FINISH_SPIN_LIMIT : (int)sp - 1;
+    spin_limit = (fs.status() != 0 || lim == 0) ? -1 : lim;
   }
   __syncthreads();
   const uint32_t tg = block_tag;
@@ -238,7 +296,9 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
     float v = -INFINITY;
     int r = INT_MAX;
     int id = 0, id_row = -1;  // dh_idx[id_row] (batch 1: after each round)
-    for (int i0 = threadIdx.x; i0 < nblk; i0 += NT * UNR) {
+    if (spin_limit < 0 && threadIdx.x == 0) failed = 1;
+    for (int i0 = threadIdx.x; spin_limit >= 0 && i0 < nblk;
+         i0 += NT * UNR) {
       uint32_t pending = 0;
       const FinishSlot* ps[UNR];
 #pragma unroll
@@ -287,7 +347,7 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
         if (pending == 0) break;
         issue(v0, r0);
         check(v1, r1);
-        if (pending != 0 && spin >= FINISH_SPIN_LIMIT) {
+        if (pending != 0 && spin >= spin_limit) {
           failed = 1;
           break;
         }
@@ -315,9 +375,13 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
       if (r == fr)
         a.out_ids[b] = failed ? -1 : (id_row == r ? id : a.dh_idx[fr]);
     } else if (threadIdx.x == 0) {
-      // no row won: only reachable when every logit is NaN
+      // no row won: only reachable when every logit is NaN (or when the
+      // collector gave up before its first poll)
       a.out_ids[b] = failed ? -1 : a.dh_idx[0];
     }
+    if (failed && threadIdx.x == 0)  // the status half of the dword at 4
+      __hip_atomic_fetch_or(reinterpret_cast<uint32_t*>(a.ws + WS_STATUS), 1u,
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();  // cv/cr are reused by the next column
   }
   // The last block collects column 0, so it has seen every block's slot, and
@@ -334,7 +398,7 @@ template <int B, int NT>
 __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
                                               int (&best_r)[B],
                                               const KArgs& a,
-                                              uint32_t epoch) {
+                                              const FinishState& st) {
   static_assert((B & (B - 1)) == 0, "batch slots are a power of two");
   __shared__ WaveBest<B, NT> w;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -346,7 +410,7 @@ __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
       w.r[wave][b] = best_r[b];
     }
   }
-  finish_from_waves<B, NT>(w, a, epoch);
+  finish_from_waves<B, NT>(w, a, st);
 }
 
 // MFMA output layout: the 16 lanes of row q = lane / 16 hold the candidates
@@ -356,7 +420,7 @@ template <int NT>
 __device__ __forceinline__ void argmax_finish_rows(float (&best_v)[4],
                                                    int (&best_r)[4],
                                                    const KArgs& a,
-                                                   uint32_t epoch) {
+                                                   const FinishState& st) {
   __shared__ WaveBest<16, NT> w;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -367,7 +431,7 @@ __device__ __forceinline__ void argmax_finish_rows(float (&best_v)[4],
       w.r[wave][4 * (lane >> 4) + j] = best_r[j];
     }
   }
-  finish_from_waves<16, NT>(w, a, epoch);
+  finish_from_waves<16, NT>(w, a, st);
 }
 
 }  // namespace dh

@@ -2,45 +2,18 @@
 // goes to the batch-1 stream kernel (one row, a hidden size it has a shape
 // for), the MFMA kernel (two or more rows, hidden a multiple of four
 // chunks, h fits LDS) or the generic kernel, and the grid is sized to one
-// resident wave of blocks (never more blocks than work units).  The logits
-// path first fills the output with -inf (page 1, "q38_draft.py",
-// compute_logits: ids that were not kept score -inf).
+// resident wave of blocks (never more blocks than work units).  In the
+// logits modes each launch also writes -inf at the ids that were not kept
+// (page 1, "q38_draft.py", compute_logits), in the same pass (owned_ids in
+// gemv_common.h): one launch per slice.
 #include "gemv_common.h"
+
+#include <mutex>
 
 namespace dh {
 namespace {
 
-constexpr int FILL_THREADS = 256;
 constexpr int GENERIC_LDS = 64 * 1024;
-
-__global__ __launch_bounds__(FILL_THREADS) void k_fill_neg_inf(float* out,
-                                                               int64_t n) {
-  const int64_t n4 = n / 4;
-  float4* o4 = reinterpret_cast<float4*>(out);
-  const float ninf = -INFINITY;
-  const int64_t stride = (int64_t)gridDim.x * FILL_THREADS;
-  for (int64_t i = (int64_t)blockIdx.x * FILL_THREADS + threadIdx.x; i < n4;
-       i += stride)
-    o4[i] = make_float4(ninf, ninf, ninf, ninf);
-  for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * FILL_THREADS + threadIdx.x;
-       i < n; i += stride)
-    out[i] = ninf;
-}
-
-// The same fill for BF16 logits: -inf is 0xFF80, eight to a 16-byte store.
-__global__ __launch_bounds__(FILL_THREADS) void k_fill_neg_inf_bf16(
-    uint16_t* out, int64_t n) {
-  const int64_t n8 = n / 8;
-  uint4* o8 = reinterpret_cast<uint4*>(out);
-  const uint32_t w = 0xFF80FF80u;
-  const int64_t stride = (int64_t)gridDim.x * FILL_THREADS;
-  for (int64_t i = (int64_t)blockIdx.x * FILL_THREADS + threadIdx.x; i < n8;
-       i += stride)
-    o8[i] = make_uint4(w, w, w, w);
-  for (int64_t i = n8 * 8 + (int64_t)blockIdx.x * FILL_THREADS + threadIdx.x;
-       i < n; i += stride)
-    out[i] = 0xFF80u;
-}
 
 // Largest generic slice in {8,4,2,1} that fits the remaining rows and LDS.
 int generic_slice(int64_t remaining, int64_t hidden) {
@@ -53,6 +26,58 @@ int out_mode(const GemvArgs& ga) {
   if (ga.out_logits == nullptr) return ga.bf16_logits ? OUT_TOP_BF16 : OUT_TOP;
   if (ga.dense) return OUT_DENSE;
   return ga.bf16_logits ? OUT_SCATTER_BF16 : OUT_SCATTER;
+}
+
+// Blocks of a kernel shape that fit one CU, queried once per (kernel, block
+// size, dynamic LDS, device) and kept.  A kernel that needs more than 64 KB
+// of dynamic LDS has its limit raised the first time, and raised again
+// only when a later shape needs more (the limit never shrinks, so a cached
+// shape stays launchable).  The lock makes the tables safe for concurrent
+// host threads; the queries are a few microseconds, the lookup is not.
+hipError_t occupancy(const KernelDesc& d, int dev, int* occ) {
+  struct Occ {
+    const void* fn;
+    int dev, threads;
+    size_t lds;
+    int occ;
+  };
+  struct Lim {
+    const void* fn;
+    int dev;
+    size_t lds;
+  };
+  constexpr int N = 512;
+  static std::mutex mu;
+  static Occ occs[N];
+  static Lim lims[N];
+  static int n_occ = 0, n_lim = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n_occ; ++i)
+    if (occs[i].fn == d.fn && occs[i].dev == dev &&
+        occs[i].threads == d.threads && occs[i].lds == d.lds_bytes) {
+      *occ = occs[i].occ;
+      return hipSuccess;
+    }
+  hipError_t e;
+  if (d.lds_bytes > 64 * 1024) {
+    int li = 0;
+    while (li < n_lim && !(lims[li].fn == d.fn && lims[li].dev == dev)) ++li;
+    if (li == n_lim || lims[li].lds < d.lds_bytes) {
+      e = hipFuncSetAttribute(d.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)d.lds_bytes);
+      if (e != hipSuccess) return e;
+      if (li == n_lim && n_lim < N) ++n_lim;
+      if (li < N) lims[li] = Lim{d.fn, dev, d.lds_bytes};
+    }
+  }
+  int o = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, d.fn, d.threads,
+                                                   d.lds_bytes);
+  if (e != hipSuccess) return e;
+  if (o < 1) o = 1;
+  if (n_occ < N) occs[n_occ++] = Occ{d.fn, dev, d.threads, d.lds_bytes, o};
+  *occ = o;
+  return hipSuccess;
 }
 
 hipError_t plan_slice(const GemvArgs& ga, int64_t remaining,
@@ -84,32 +109,14 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
   const bool logits = ga.out_logits != nullptr;
-  if (logits && !ga.dense) {
-    const int64_t n = ga.batch * ga.vocab;
-    int64_t blocks = (n / 4 + FILL_THREADS - 1) / FILL_THREADS;
-    if (blocks > (int64_t)di.cus * 8) blocks = (int64_t)di.cus * 8;
-    if (blocks < 1) blocks = 1;
-    if (ga.bf16_logits)
-      k_fill_neg_inf_bf16<<<(int)blocks, FILL_THREADS, 0, s>>>(
-          reinterpret_cast<uint16_t*>(ga.out_logits), n);
-    else
-      k_fill_neg_inf<<<(int)blocks, FILL_THREADS, 0, s>>>(ga.out_logits, n);
-  }
   for (int64_t b0 = 0; b0 < ga.batch;) {
     KernelDesc d;
     int bc = 0;
     e = plan_slice(ga, ga.batch - b0, di, &d, &bc);
     if (e != hipSuccess) return e;
-    if (d.lds_bytes > 64 * 1024) {
-      e = hipFuncSetAttribute(d.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)d.lds_bytes);
-      if (e != hipSuccess) return e;
-    }
     int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, d.fn, d.threads,
-                                                     d.lds_bytes);
+    e = occupancy(d, di.dev, &occ);
     if (e != hipSuccess) return e;
-    if (occ < 1) occ = 1;
     const int waves = d.threads / 64;
     const int64_t units = ga.n_rows / d.rows_per_unit;
     int64_t grid = (int64_t)di.cus * occ;

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
   constexpr int HD = F::EPU / 2;  // h dwords per unit
   extern __shared__ uint4 hs4[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t epoch = LOGITS ? 0u : finish_epoch(a);
+  const FinishState st = LOGITS ? FinishState{} : finish_state(a);
   {
     const uint4* src = reinterpret_cast<const uint4*>(a.h);
     const int n = (int)(B * a.hidden / 8);
@@ -50,13 +50,30 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
       for (int b = 0; b < B; ++b)
         acc[b] = F::unit_dot(p, s, hs + b * (a.hidden / 2) + c * HD, acc[b]);
     }
+    if constexpr (is_scatter(MODE)) {
+      // the row's logits at its id and -inf over the ids it owns
+      // (owned_ids): the wave writes them for every batch row
+      if (row < a.n_kept) {  // wave-uniform
+        const int32_t id = a.dh_idx[row];
+        const IdRange rg = owned_ids(row, 1, row > 0 ? a.dh_idx[row - 1] : 0,
+                                     id, a.n_kept, a.vocab);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float v = group_sum<64>(acc[b]) *
+                          (a.row_scale ? sc * a.row_scale[b] : sc);
+          for (int64_t p = rg.lo + lane; p < rg.hi; p += 64)
+            store_logit<MODE>(a.out_logits, b * a.vocab + p,
+                              p == id ? v : not_kept_value<MODE>());
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const float v = group_sum<64>(acc[b]);
-      if constexpr (LOGITS) {
-        if (lane == 0 && row < a.n_kept)
-          store_logit<MODE>(a.out_logits,
-                            b * a.vocab + out_col<MODE>(a.dh_idx, row),
+      if constexpr (MODE == OUT_DENSE) {
+        if (lane == 0)
+          store_logit<MODE>(a.out_logits, b * a.vocab + row,
                             v * (a.row_scale ? sc * a.row_scale[b] : sc));
       } else {
         const float c = top_value<MODE>(v, sc);
@@ -67,7 +84,7 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
       }
     }
   }
-  if constexpr (!LOGITS) argmax_finish<B, THREADS>(best_v, best_r, a, epoch);
+  if constexpr (!LOGITS) argmax_finish<B, THREADS>(best_v, best_r, a, st);
 }
 
 template <class F, int L>

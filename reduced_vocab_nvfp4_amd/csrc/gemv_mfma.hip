@@ -52,7 +52,11 @@ struct Slot {
   uint4 p[RT][SPS];
   uint32_t s[RT][wide_scales<F, SPS>() ? 1 : SPS];
   uint4 sw[RT][wide_scales<F, SPS>() ? SPS / 2 : 1];
-  int32_t ids[RT];  // dh_idx of the tile rows (logits path)
+  // scatter modes: lane l holds dh_idx[r0 - 1 + min(l, 16)] of tile t (r0
+  // its first row; row -1 reads row 0): the kept id before the tile, then
+  // the tile's 16 ids.  The address depends on the lane, so this is a
+  // vector load, which the prologue's wait count relies on.
+  int32_t ids[RT];
 };
 
 // The two scale bytes of step C for a lane of k-slot group q.
@@ -103,6 +107,51 @@ __device__ __forceinline__ void slot_steps(const Slot<F, RT, SPS>& b, int q,
   }
 }
 
+// Logits of one 16-row tile (scatter modes), written by the whole wave: the
+// id range the tile's kept rows own (owned_ids in gemv_common.h), each batch
+// row's logit at its row's id and -inf between them.  Lane l holds
+// id = dh_idx[r0 - 1 + min(l, 16)] (Slot::ids) and, in register j, the
+// scaled logit of batch row 4(l/16) + j and tile row l%16 (the MFMA output
+// layout).  For a position p of the range, the kept rows below it are
+// counted against the tile's ids (ascending), which names the only row
+// that can hold p; its logits come over with ds_bpermute.
+template <int MODE>
+__device__ __forceinline__ void scatter_tile(const KArgs& a, int64_t r0,
+                                             int32_t id, const f32x4& val,
+                                             int nb) {
+  if (r0 >= a.n_kept) return;  // pad rows only
+  const int64_t left = a.n_kept - r0;
+  const int nk = left < 16 ? (int)left : 16;
+  int32_t ids[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ids[i] = __builtin_amdgcn_readlane(id, i + 1);
+  const IdRange rg =
+      owned_ids(r0, nk, __builtin_amdgcn_readlane(id, 0),
+                __builtin_amdgcn_readlane(id, nk), a.n_kept, a.vocab);
+  const int lane = (int)(threadIdx.x & 63);
+  for (int64_t p0 = rg.lo; p0 < rg.hi; p0 += 64) {
+    const int p = (int)(p0 + lane);  // vocab <= INT32_MAX
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cnt += (i < nk && ids[i] < p) ? 1 : 0;
+    const int c = cnt < 15 ? cnt : 15;
+    // every ds_bpermute runs with the whole wave active: a lane reading from
+    // a lane the exec mask left out would get 0
+    const int at = __builtin_amdgcn_ds_bpermute(4 * (c + 1), id);
+    const bool kept = cnt < nk && at == p;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      if (m < nb) {  // wave-uniform
+        const float lv = __int_as_float(__builtin_amdgcn_ds_bpermute(
+            4 * ((m >> 2) * 16 + c), __float_as_int(val[m & 3])));
+        if (p < rg.hi)
+          store_logit<MODE>(a.out_logits, (int64_t)m * a.vocab + p,
+                            kept ? lv : not_kept_value<MODE>());
+      }
+    }
+  }
+}
+
 template <class F, int RT, int SPS, int NB, int MODE, int NT>
 __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   constexpr bool LOGITS = !is_top(MODE);
@@ -112,7 +161,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t epoch = LOGITS ? 0u : finish_epoch(a);
+  const FinishState st = LOGITS ? FinishState{} : finish_state(a);
   const int64_t hidden = a.hidden;
   const int nb = a.nb;
 
@@ -190,9 +239,13 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
                 *reinterpret_cast<const uint16_t*>(sb + soff[t] + 8 * c);
           }
     }
-    if constexpr (MODE == OUT_SCATTER || MODE == OUT_SCATTER_BF16) {
+    if constexpr (is_scatter(MODE)) {
+      const int64_t l = lane < 16 ? lane : 16;
 #pragma unroll
-      for (int t = 0; t < RT; ++t) b.ids[t] = a.dh_idx[row0 + 16 * t + n];
+      for (int t = 0; t < RT; ++t) {
+        const int64_t j = row0 + 16 * t - 1 + l;
+        b.ids[t] = a.dh_idx[j > 0 ? j : 0];
+      }
     }
     // The cursor stops at the wave's last slot: the surplus loads of the
     // padded ring re-read it (L2 hits) and are never computed.
@@ -208,13 +261,27 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   f32x4 acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // logits factor of batch row 4q + j (rows past the slice are never
-  // written)
-  float lsc[4];
+  // Logits factor of batch row 4q + j (rows past the slice are never
+  // written): the tensor scale times the row's own scale.  Both are loaded
+  // here and first used when a unit completes (lane_scales), so their
+  // latency hides behind the loop instead of delaying the first loads.
+  const float tsc = MODE != OUT_TOP ? tensor_scale(a) : 1.0f;
+  float rsc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    lsc[j] = MODE != OUT_TOP && 4 * q + j < nb ? logit_scale(a, 4 * q + j)
-                                                : 1.0f;
+  for (int j = 0; j < 4; ++j) {
+    const int m = 4 * q + j < nb ? 4 * q + j : nb - 1;
+    rsc[j] = MODE != OUT_TOP && a.row_scale ? a.row_scale[m] : 1.0f;
+  }
+  // (the empty asm keeps the compiler from forming the products, and so
+  // waiting for the loads, before the loop)
+  auto lane_scales = [&](float (&lsc)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float t = tsc, r = rsc[j];
+      asm volatile("" : "+v"(t), "+v"(r));
+      lsc[j] = t * r;
+    }
+  };
   float best_v[4];
   int best_r[4];
 #pragma unroll
@@ -229,28 +296,19 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   // zero row is written, and the first weight slots are issued, so the
   // staging overlaps their latency.  Memory loads retire in issue order:
   // once no more than the weight loads are outstanding, this wave's copies
-  // have landed; the barrier then covers every wave's.  (The copies are inline
-  // assembly with an explicit wait: the compiler does not order LDS reads
-  // after global_load_lds on its own, and a __syncthreads fence would also
-  // wait for the weight loads.  The clobber of M0, a register the compiler
-  // reserves and sets right before each instruction that reads it, draws a
-  // warning and is all the compiler needs to know.)
+  // have landed; the barrier then covers every wave's.  (The wait is
+  // explicit, see lds_copy_x4; a __syncthreads fence would also wait for the
+  // weight loads.)
   {
     const char* hb = reinterpret_cast<const char*>(a.h);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(
-        (__attribute__((address_space(3))) void*)hs);
+    const uint32_t lds_base = lds_addr(hs);
     const int pieces = nb * PPR;
     for (int pc = wv; pc < pieces; pc += NW) {
       const int r = pc / PPR, j = pc - r * PPR;
       const int off = j * 1024 + 16 * lane;
       const int src = off < RBH ? off : RBH - 16;
-      asm volatile(
-          "s_mov_b32 m0, %1\n\t"
-          "global_load_lds_dwordx4 %0, off"
-          :
-          : "v"(hb + (int64_t)r * RBH + src),
-            "s"(lds_base + (uint32_t)(r * SB + j * 1024))
-          : "memory", "m0");
+      lds_copy_x4(hb + (int64_t)r * RBH + src,
+                  lds_base + (uint32_t)(r * SB + j * 1024));
     }
     uint4* zrow = hs + nb * (SB / 16);
     for (int i = threadIdx.x; i < SB / 16; i += NT)
@@ -268,8 +326,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   constexpr int SCALE_LOADS =
       wide_scales<F, SPS>() ? SPS / 2 : (F::SCALED ? SPS : 0);
   constexpr int WEIGHT_LOADS =
-      (NB - 1) * (RT * (SPS + SCALE_LOADS) +
-                  (MODE == OUT_SCATTER || MODE == OUT_SCATTER_BF16 ? RT : 0));
+      (NB - 1) * (RT * (SPS + SCALE_LOADS) + (is_scatter(MODE) ? RT : 0));
   static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(WEIGHT_LOADS)
@@ -290,18 +347,28 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
         if (cp_js == js1 - 1) {
           // unit done: rows row0 + 16t + n, batch rows 4q + j (a split
           // unit's parts are added after the loop)
+          float lsc[4];
+          lane_scales(lsc);
+          if constexpr (is_scatter(MODE)) {
 #pragma unroll
-          for (int t = 0; t < RT && ks == 1; ++t) {
+            for (int t = 0; t < RT; ++t) {
+              f32x4 sv;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sv[j] = acc[t][j] * lsc[j];
+              scatter_tile<MODE>(a, cp_row0 + 16 * t, b.ids[t], sv, nb);
+              acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < RT && ks == 1 && !is_scatter(MODE); ++t) {
             const int64_t row = cp_row0 + 16 * t + n;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float v = acc[t][j];
-              if constexpr (LOGITS) {
+              if constexpr (MODE == OUT_DENSE) {
                 const int m = 4 * q + j;
                 if (m < nb && row < a.n_kept)
-                  store_logit<MODE>(a.out_logits,
-                                    (int64_t)m * a.vocab +
-                                        (MODE == OUT_DENSE ? row : b.ids[t]),
+                  store_logit<MODE>(a.out_logits, (int64_t)m * a.vocab + row,
                                     v * lsc[j]);
               } else {
                 const float c = top_value<MODE>(v, lsc[j]);
@@ -332,6 +399,8 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
       for (int t = 0; t < RT; ++t) red[(wv * RT + t) * 64 + lane] = acc[t];
       __syncthreads();
       if (kp == 0 && n_u > 0) {
+        float lsc[4];
+        lane_scales(lsc);
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           f32x4 v = acc[t];
@@ -353,7 +422,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   }
   if constexpr (!LOGITS) {
     // batch row b lives in register b%4 of the lanes with l/16 == b/4
-    argmax_finish_rows<NT>(best_v, best_r, a, epoch);
+    argmax_finish_rows<NT>(best_v, best_r, a, st);
   }
 }
 

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(dh.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared but not exported"
-    assert dh.lib().drafthead_abi_version() == 2
+    assert dh.lib().drafthead_abi_version() == 3
     assert dh.error_string(dh.DH_EINVAL).startswith("invalid")
 
 

@@ -187,9 +187,11 @@ def stock():
 
 @pytest.mark.parametrize("batch", [1, 4])
 def test_bf16_stock_top_tokens(batch):
+    """The stock 248 320 x 2560 BF16 head: sixteen hidden states at batch 1
+    (the stock-head workload), one batch of four."""
     hd = stock()
     exc = 0
-    for s in range(3 if batch == 1 else 1):
+    for s in range(16 if batch == 1 else 1):
         h = wl.hidden_states(batch, hd.hidden, 60 + s)
         ids = dh.draft_head_top_tokens_bf16(hd.w_gpu, hd.idx_gpu,
                                             h.to(DEV)).cpu().numpy()
@@ -264,15 +266,26 @@ def test_nvfp4_top_tokens_h98k_b16():
     assert exc <= 1
 
 
-def test_nvfp4_dense27b_b8_top_tokens_and_logits():
+def test_nvfp4_dense27b_b8_top_tokens_and_logits_16_draws():
+    """The 27B-shaped head (64 064 x 5120 NVFP4) at batch 8: sixteen seeded
+    batches, the ids and every logit of the full-vocabulary output of each
+    against the oracle."""
     hd = nvfp4_head("dense27b_64k_b8")
-    h = wl.hidden_states(8, hd.hidden, 0)
-    assert _nvfp4_top_check(hd, h, "dense27b B=8") <= 1
-    out = dh.draft_head_logits(hd.packed, hd.scales, hd.gs, hd.idx_gpu,
-                               hd.n_kept, hd.vocab, h.to(DEV)).cpu().numpy()
-    ref = oracle.logits_scatter(hd.oracle_logits(h), hd.n_kept, hd.idx,
-                                hd.vocab)
-    _logits_ok(out, ref, "dense27b B=8")
+    exc = 0
+    for s in range(16):
+        h = wl.hidden_states(8, hd.hidden, s)
+        L = hd.oracle_logits(h)
+        ids = dh.draft_head_top_tokens(hd.packed, hd.scales, hd.gs,
+                                       hd.idx_gpu, h.to(DEV)).cpu().numpy()
+        _, want = oracle.argmax_remap(L, hd.idx)
+        exc += H.check_top_tokens(ids, L, hd.idx, hd.n_kept, want)
+        out = dh.draft_head_logits(hd.packed, hd.scales, hd.gs, hd.idx_gpu,
+                                   hd.n_kept, hd.vocab,
+                                   h.to(DEV)).cpu().numpy()
+        _logits_ok(out, oracle.logits_scatter(L, hd.n_kept, hd.idx, hd.vocab),
+                   f"dense27b B=8 s{s}")
+    say(f"[nvfp4] dense27b: 16 batches of 8, near-tie exceptions {exc}")
+    assert exc <= 2
 
 
 # ------------------------------------------------ shapes of every kernel

@@ -54,3 +54,32 @@ def test_concurrent_calls_on_separate_streams():
         assert torch.equal(outs_b[i], ref_b[i]), i
         assert torch.equal(outs_t[i], ref_t[i]), i
         assert torch.equal(outs_8[i], ref_8[i]), i
+
+
+def test_calls_on_a_side_stream_allocate_there():
+    """stream= without a workspace or outputs: the binding allocates them on
+    that stream, so the workspace's zero-fill is ordered before the kernels
+    and the memory is not handed to other work while they run.  The current
+    stream is kept busy meanwhile (a long device sleep), so work wrongly
+    ordered on it would come after the side stream's kernels."""
+    tiny = head("tiny")
+    w = tiny.w_gpu
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    hs = [wl.hidden_states(4, tiny.hidden, 1800 + i).to(DEV) for i in range(8)]
+    ref = [dh.draft_head_top_tokens(tiny.packed, tiny.scales, tiny.gs,
+                                    tiny.idx_gpu, h).clone() for h in hs]
+    ref_q = dh.nvfp4_quantize_rows(w, tiny.idx_gpu)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(5e7))  # holds the current stream
+    got = [dh.draft_head_top_tokens(tiny.packed, tiny.scales, tiny.gs,
+                                    tiny.idx_gpu, h, stream=side)
+           for h in hs]
+    q = dh.nvfp4_quantize_rows(w, tiny.idx_gpu, stream=side)
+    side.synchronize()
+    for i in range(8):
+        assert torch.equal(got[i], ref[i]), i
+    for a, b in zip(q, ref_q):
+        assert torch.equal(a, b)
+    torch.cuda.synchronize()
