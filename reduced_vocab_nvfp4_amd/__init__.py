@@ -202,8 +202,9 @@ def set_workspace_spin_limit(workspace: torch.Tensor, rounds: int) -> None:
     library's default bound."""
     if not 0 <= rounds < 0xFFFF:
         raise ValueError("rounds must be in [0, 65534]")
+    v = rounds + 1  # the uint16 field, written through a signed view
     workspace[WS_SPIN_LIMIT_OFFSET:WS_SPIN_LIMIT_OFFSET + 2].view(
-        torch.int16).fill_(rounds + 1)
+        torch.int16).fill_(v - 65536 if v >= 32768 else v)
 
 
 def new_workspace(n_rows: int, batch: int, device="cuda") -> torch.Tensor:
