@@ -549,7 +549,7 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     reps = max(1, args.repeats)
-    rep_us = []
+    rep_us, host_us = [], []
     t_wall = 0.0
     for _ in range(reps):
         torch.cuda.synchronize()
@@ -559,8 +559,12 @@ def main():
         except (AttributeError, RuntimeError):
             pass
         e0.record(stream)
+        t_host0 = time.perf_counter()
         for i in range(K):
             step(i)
+        # host time to enqueue the K calls (the device is still busy): when
+        # it exceeds the device time per step, the device waits for the host
+        host_us.append((time.perf_counter() - t_host0) * 1e6 / K)
         e1.record(stream)
         torch.cuda.synchronize()
         t_wall += time.perf_counter() - t_wall0
@@ -625,6 +629,7 @@ def main():
         "us_per_step": round(us_step, 3),
         "repeats": reps,
         "us_per_step_repeats": [round(x, 3) for x in rep_us],
+        "host_enqueue_us_per_call": round(float(np.median(host_us)), 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -79,6 +79,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
 }
 
+// Block barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt), then s_barrier.  __syncthreads also waits for every
+// outstanding vector memory operation (its workgroup release fence), which
+// in the GEMV kernels means the ring's last, unused loads: a memory round
+// trip for nothing.  The "memory" clobbers keep LDS accesses on their side.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------ reductions
 
 // DPP control words (GCN/CDNA encoding).

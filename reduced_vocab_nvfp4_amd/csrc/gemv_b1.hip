@@ -129,17 +129,28 @@ __device__ __forceinline__ void compute_rows(const Rows<F, C>& r,
     if (g == 0 && row < a.n_kept) store_logit<MODE>(a.out_logits, row, v * sc);
   } else {
     const float c = top_value<MODE>(v, sc);
-    if (c > best_v) {
-      // rows reach a lane in ascending order: strict > keeps the lowest
+    if (better(c, (int)row, best_v, best_r)) {
+      // (the waves of a block share its groups, so a lane's rows do not
+      // come in ascending order: equal values keep the lower row)
       best_v = c;
       best_r = (int)row;
     }
   }
 }
 
-// Format F, G lanes per row, C chunks per lane, NB register buffers, NT
-// threads per block.
-template <class F, int G, int C, int MODE, int NB, int NT>
+// Format F, G lanes per row, C chunks per lane, NT threads per block.
+//
+// Work: the row groups (R = 64/G rows each) are cut into one contiguous
+// slice per block, and the waves of a block take the groups of its slice
+// one at a time from a counter in LDS.  A CU's waves then finish within a
+// group of each other whatever the issue arbitration favours (with a
+// static per-wave split the oldest waves finished in half the time of the
+// youngest and the last ones streamed alone), and each block reads its
+// slice in address order.  A ring of two register buffers keeps one group
+// in flight while another is reduced: each step takes the next group's
+// index from the counter, issues its loads, then reduces the group loaded
+// one step earlier.
+template <class F, int G, int C, int MODE, int NT>
 __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   constexpr bool LOGITS = !is_top(MODE);
   constexpr int R = 64 / G;  // rows per wave iteration
@@ -147,73 +158,64 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   constexpr int HD = F::EPC / 2;           // h dwords per chunk
   constexpr int HQ = F::EPC / 8;           // h uint4 per chunk
   constexpr int HU4 = HQ * G * C;          // h as uint4
-  constexpr int HJ = (HU4 + 63) / 64;      // h copies per lane
-  __shared__ uint4 hl[NW][HJ * 64];
+  constexpr int HJ = (HU4 + 63) / 64;      // 1 KB pieces of h
+  constexpr uint32_t NONE = 0xFFFFFFFFu;   // no group left
+  __shared__ uint4 hl[HJ * 64];
+  __shared__ uint32_t next_group;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane / G, g = lane % G;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const FinishState st = LOGITS ? FinishState{} : finish_state(a);
 
-  // Row groups are dealt to the grid's waves round-robin (grid stride):
-  // wave w of the grid takes groups w, w + TW, w + 2 TW, ...  The per-wave
-  // trip count is wave-uniform so loop control stays scalar.
+  // The block's slice [g0, g0 + NG) of the T row groups; the host launches
+  // no more blocks than groups, so NG >= 1.
   const int64_t T = a.n_rows / R;
-  const int64_t TW = (int64_t)gridDim.x * NW;
-  const int64_t first = (int64_t)blockIdx.x * NW + wv;
-  const int n_it = first < T ? (int)((T - first + TW - 1) / TW) : 0;
-
-  // A ring of NB register buffers: the loads of group it+NB-1 are issued
-  // before group it is reduced, so NB-1 groups stay in flight.  The trip
-  // count is rounded up to a multiple of NB and row indices past the wave's
-  // last group are clamped to it: every load in the loop is unconditional
-  // (which keeps the compiler's wait counts exact) and the surplus loads hit
-  // in L2; the reduction of those padded iterations is skipped.
-  // (A wave without row groups, possible only on tiny heads, reads group 0
-  // in its prologue and never reduces it.)
-  const int n_pad = (n_it + NB - 1) / NB * NB;
-  const int64_t base = n_it > 0 ? first : 0;
-  const int last = n_it > 0 ? n_it - 1 : 0;
-  auto row0_of = [&](int it) {  // first row of the group (wave-uniform)
-    const int c = it < last ? it : last;
-    return (base + (int64_t)c * TW) * R;
-  };
+  const int64_t g0 = (int64_t)blockIdx.x * T / gridDim.x;
+  const uint32_t NG =
+      (uint32_t)((int64_t)(blockIdx.x + 1) * T / gridDim.x - g0);
   const uint32_t lane_chunk = (uint32_t)(grp * G * C + g);
-  // Prologue.  h is copied straight into this wave's LDS slice with
-  // global_load_lds_dwordx4 (lane i's 16 bytes land at slice + 16*i; no
-  // VGPRs, no block barrier), then the first weight row groups are issued,
-  // so only h has to arrive before the ring starts.  Every lane then keeps
-  // its C chunks of h in VGPRs.
+  auto row0_of = [&](uint32_t gi) { return (g0 + gi) * R; };
+
+  // Prologue.  The block's one copy of h goes straight into LDS with
+  // global_load_lds_dwordx4, a 1 KB piece per wave (lane i's 16 bytes land
+  // at piece + 16*i; lanes past the end of h re-read its last uint4 into
+  // the slack).  Wave w then issues the loads of group w; its explicit
+  // wait covers its own copies (vector loads retire in issue order), and
+  // the barrier covers every wave's.  The counter starts past the groups
+  // the waves took here.
+  // Every wave issues the same number of copies, in straight-line code
+  // (pieces past the last are clamped to it: a second copy of the same
+  // bytes), so the compiler keeps them ahead of the weight loads that the
+  // explicit wait below counts.
   const uint4* h4 = reinterpret_cast<const uint4*>(a.h);
+  constexpr int CPW = (HJ + NW - 1) / NW;  // copies per wave
 #pragma unroll
-  for (int j = 0; j < HJ; ++j) {
-    // lanes past the end of h (when HU4 % 64 != 0) re-read its last uint4
-    // into the slack of the slice
+  for (int t = 0; t < CPW; ++t) {
+    const int j = wv + NW * t < HJ ? wv + NW * t : HJ - 1;
     const int src = (HU4 % 64 == 0 || 64 * j + lane < HU4) ? 64 * j + lane
                                                             : HU4 - 1;
-    lds_copy_x4(h4 + src, lds_addr(&hl[wv][64 * j]));
+    lds_copy_x4(h4 + src, lds_addr(&hl[64 * j]));
   }
+  if (threadIdx.x == 0) next_group = NW;
   __builtin_amdgcn_sched_barrier(0);
-  Rows<F, C> buf[NB];
-#pragma unroll
-  for (int k = 0; k < NB - 1; ++k)
-    load_rows<F, G, C, MODE>(buf[k], a, row0_of(k), lane_chunk);
-  // Memory loads retire in issue order, so once no more than the weight
-  // loads just issued are outstanding, the h copies have landed in LDS.
-  // (The wait is explicit: the compiler does not order LDS reads after
-  // global_load_lds on its own.)  The "memory" clobber keeps the LDS reads
-  // below it.
+  Rows<F, C> buf[2];
+  uint32_t gi[2];
+  gi[0] = (uint32_t)wv < NG ? (uint32_t)wv : NONE;
+  load_rows<F, G, C, MODE>(buf[0], a, row0_of(gi[0] != NONE ? gi[0] : NG - 1),
+                           lane_chunk);
   constexpr int WEIGHT_LOADS =
-      (NB - 1) * ((F::SCALED ? 2 : 1) * C + (is_scatter(MODE) ? 1 : 0));
+      (F::SCALED ? 2 : 1) * C + (is_scatter(MODE) ? 1 : 0);
   static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WEIGHT_LOADS) : "memory");
+  lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   uint32_t hreg[C * HD];
 #pragma unroll
   for (int i = 0; i < C; ++i) {
 #pragma unroll
     for (int q = 0; q < HQ; ++q) {
-      const uint4 v = hl[wave][(g + G * i) * HQ + q];
+      const uint4 v = hl[(g + G * i) * HQ + q];
       hreg[i * HD + 4 * q + 0] = v.x;
       hreg[i * HD + 4 * q + 1] = v.y;
       hreg[i * HD + 4 * q + 2] = v.z;
@@ -223,47 +225,63 @@ __global__ __launch_bounds__(NT) void k_b1(const KArgs a) {
   const float sc = MODE != OUT_TOP ? logit_scale(a, 0) : 1.0f;
   float best_v = -INFINITY;
   int best_r = INT_MAX;
-
-  if (n_it > 0) {
-    for (int it = 0; it < n_pad; it += NB) {
+  // next group of the slice, or NONE (one LDS atomic per wave and step)
+  auto take = [&]() {
+    uint32_t n = 0;
+    if (lane == 0)
+      n = __hip_atomic_fetch_add(&next_group, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+    n = __builtin_amdgcn_readfirstlane(n);
+    return n < NG ? n : NONE;
+  };
+  // The ring: step k issues the loads of the next group into the buffer
+  // freed one step earlier, then reduces buffer k.  Groups come from the
+  // counter in increasing order, so the first NONE ends the wave's work.
+  // Every step loads (a NONE step re-reads the slice's last group, an L2
+  // hit that is never reduced): loads that depend on the counter would cost
+  // the loop exact wait counts.
+  bool live = gi[0] != NONE;
+  while (live) {
 #pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        load_rows<F, G, C, MODE>(buf[(k + NB - 1) % NB], a,
-                                 row0_of(it + k + NB - 1), lane_chunk);
-        __builtin_amdgcn_sched_barrier(0);
-        if (it + k < n_it)  // wave-uniform: padded iterations only load
-          compute_rows<F, G, C, MODE>(buf[k], a, row0_of(it + k) + grp, g,
-                                        hreg, sc,
-                                        best_v, best_r);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t nx = take();
+      gi[1 - k] = nx;
+      load_rows<F, G, C, MODE>(buf[1 - k], a,
+                               row0_of(nx != NONE ? nx : NG - 1), lane_chunk);
+      __builtin_amdgcn_sched_barrier(0);
+      if (gi[k] == NONE) {
+        live = false;
+        break;
       }
+      compute_rows<F, G, C, MODE>(buf[k], a, row0_of(gi[k]) + grp, g, hreg,
+                                  sc, best_v, best_r);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if constexpr (!LOGITS) {
     float bv[1] = {best_v};
     int br[1] = {best_r};
-    argmax_finish<1, NT>(bv, br, a, st);
+    // 2 slots per thread: the grid is two 256-thread blocks per CU
+    argmax_finish<1, NT, 2>(bv, br, a, st);
   }
 }
 
-// Kernel shape: two register buffers, 256-thread blocks (the occupancy
-// query then fits three blocks per CU at <= 168 VGPRs).
-constexpr int RING = 2;
+// Kernel shape: 256-thread blocks, two per CU (eight waves per CU; a third
+// block measured slower: its waves start late and its extra loads buy no
+// bandwidth).
 constexpr int B1_THREADS = 256;
+constexpr int B1_BLOCKS_PER_CU = 2;
 
-// Static LDS of the per-wave h slices must stay within 64 KB.
 template <class F, int G, int C>
 constexpr bool fits() {
-  return (B1_THREADS / 64) * (((F::EPC / 8) * G * C + 63) / 64) * 64 * 16 <=
-         64 * 1024;
+  return (((F::EPC / 8) * G * C + 63) / 64) * 64 * 16 <= 64 * 1024;
 }
 
 template <class F, int G, int C, int L>
 bool desc(KernelDesc* d) {
   if constexpr (fits<F, G, C>()) {
-    *d = KernelDesc{reinterpret_cast<const void*>(
-                        k_b1<F, G, C, L, RING, B1_THREADS>),
-                    B1_THREADS, 64 / G, 0, false};
+    *d = KernelDesc{reinterpret_cast<const void*>(k_b1<F, G, C, L, B1_THREADS>),
+                    B1_THREADS, 64 / G, 0, false, 0, B1_BLOCKS_PER_CU};
     return true;
   }
   return false;

@@ -124,6 +124,7 @@ struct KernelDesc {
   bool spread;        // units dealt wave-major: one block per unit suffices
   int split_slots;    // > 0: the waves of a block may split a unit's
                       // split_slots slots over the hidden dimension
+  int per_cu;         // > 0: blocks per CU to launch (else as many as fit)
 };
 
 // Kernel families; each returns false when it has no kernel for the shape.
@@ -229,8 +230,11 @@ struct WaveBest {
   int r[NT / 64][B];
 };
 
-// The block's part once every wave has put its per-column best in w.
-template <int B, int NT>
+// The block's part once every wave has put its per-column best in w.  A
+// collecting thread polls UNR slots per round: the kernel picks it so that
+// one round covers its usual grid (the slot count) with NT threads and no
+// thread loads a slot twice.
+template <int B, int NT, int UNR>
 __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
                                                   const KArgs& a,
                                                   const FinishState& st) {
@@ -259,7 +263,7 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
     const int lim = sp == 0 ? FINISH_SPIN_LIMIT : (int)sp - 1;
     spin_limit = (fs.status() != 0 || lim == 0) ? -1 : lim;
   }
-  __syncthreads();
+  lds_barrier();  // LDS only: see lds_barrier
   const uint32_t tg = block_tag;
   if (threadIdx.x < B) {
     const int b = threadIdx.x;
@@ -282,16 +286,16 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
   // from different CUs (the uncached polling loads of one CU are served one
   // after another), and the collectors are the blocks dispatched last,
   // which tend to finish last, so most slots are there by their first poll.
-  // Thread t polls the slots of blocks t + k * NT, UNR of them per round.
+  // Thread t polls the slots of blocks t + k * NT, UNR of them per round
+  // (further rounds if the grid has more than NT * UNR blocks).
   // Two rounds are in flight: round k+1 is issued before round k is
   // checked.  Every load of a round is issued whether or not its slot is
-  // still pending (slot indices past the grid are clamped to the last slot,
-  // and their results ignored), so the number of loads outstanding is the
-  // same on every path and the wait before a check covers only the older
-  // round.
+  // still pending (slot indices past the grid wrap to one of the thread's
+  // own slots, and their results are ignored), so the number of loads
+  // outstanding is the same on every path and the wait before a check
+  // covers only the older round.
   const int nblk = (int)gridDim.x;
   const int ncol = a.nb < B ? a.nb : B;
-  constexpr int UNR = 4;
   for (int b = nblk - 1 - (int)blockIdx.x; b < ncol; b += nblk) {
     float v = -INFINITY;
     int r = INT_MAX;
@@ -305,7 +309,10 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
       for (int u = 0; u < UNR; ++u) {
         const int i = i0 + u * NT;
         if (i < nblk) pending |= 1u << u;
-        ps[u] = slot + (int64_t)(i < nblk ? i : nblk - 1) * B + b;
+        // past the grid: one of this thread's own slots again (a second
+        // load of a line it polls anyway; a common clamp to the last slot
+        // sends every thread's surplus loads to one address)
+        ps[u] = slot + (int64_t)(i < nblk ? i : i % nblk) * B + b;
       }
       uint64_t v0[UNR], r0[UNR], v1[UNR], r1[UNR];
       auto issue = [&](uint64_t (&tv)[UNR], uint64_t (&tr)[UNR]) {
@@ -363,7 +370,7 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
       cv[wave] = wvv;
       cr[wave] = wr;
     }
-    __syncthreads();
+    lds_barrier();
     float fv = cv[0];
     int fr = cr[0];
     for (int w = 1; w < NW; ++w)
@@ -382,7 +389,7 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
     if (failed && threadIdx.x == 0)  // the status half of the dword at 4
       __hip_atomic_fetch_or(reinterpret_cast<uint32_t*>(a.ws + WS_STATUS), 1u,
                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();  // cv/cr are reused by the next column
+    lds_barrier();  // cv/cr are reused by the next column
   }
   // The last block collects column 0, so it has seen every block's slot, and
   // with it every block's read of the counter, before it advances the
@@ -394,7 +401,7 @@ __device__ __forceinline__ void finish_from_waves(const WaveBest<B, NT>& w,
 
 // Every lane holds a candidate for each of the B columns: one wave argmax
 // per column.
-template <int B, int NT>
+template <int B, int NT, int UNR>
 __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
                                               int (&best_r)[B],
                                               const KArgs& a,
@@ -410,13 +417,13 @@ __device__ __forceinline__ void argmax_finish(float (&best_v)[B],
       w.r[wave][b] = best_r[b];
     }
   }
-  finish_from_waves<B, NT>(w, a, st);
+  finish_from_waves<B, NT, UNR>(w, a, st);
 }
 
 // MFMA output layout: the 16 lanes of row q = lane / 16 hold the candidates
 // of columns 4q + j in register j.  Four 16-lane DPP reductions, which run
 // on the four rows at once, replace sixteen whole-wave ones.
-template <int NT>
+template <int NT, int UNR>
 __device__ __forceinline__ void argmax_finish_rows(float (&best_v)[4],
                                                    int (&best_r)[4],
                                                    const KArgs& a,
@@ -431,7 +438,7 @@ __device__ __forceinline__ void argmax_finish_rows(float (&best_v)[4],
       w.r[wave][4 * (lane >> 4) + j] = best_r[j];
     }
   }
-  finish_from_waves<16, NT>(w, a, st);
+  finish_from_waves<16, NT, UNR>(w, a, st);
 }
 
 }  // namespace dh

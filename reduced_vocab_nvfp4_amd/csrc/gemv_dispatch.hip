@@ -117,6 +117,7 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     int occ = 0;
     e = occupancy(d, di.dev, &occ);
     if (e != hipSuccess) return e;
+    if (d.per_cu > 0 && d.per_cu < occ) occ = d.per_cu;
     const int waves = d.threads / 64;
     const int64_t units = ga.n_rows / d.rows_per_unit;
     int64_t grid = (int64_t)di.cus * occ;

@@ -84,7 +84,9 @@ __global__ __launch_bounds__(THREADS) void k_generic(const KArgs a) {
       }
     }
   }
-  if constexpr (!LOGITS) argmax_finish<B, THREADS>(best_v, best_r, a, st);
+  // 4 slots per thread: the grid may hold several blocks per CU
+  if constexpr (!LOGITS)
+    argmax_finish<B, THREADS, 4>(best_v, best_r, a, st);
 }
 
 template <class F, int L>

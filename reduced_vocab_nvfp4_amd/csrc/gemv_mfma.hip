@@ -422,7 +422,9 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   }
   if constexpr (!LOGITS) {
     // batch row b lives in register b%4 of the lanes with l/16 == b/4
-    argmax_finish_rows<NT>(best_v, best_r, a, st);
+    // one slot per thread: the grid is one block (512 or 1024 threads) per
+    // CU
+    argmax_finish_rows<NT, 1>(best_v, best_r, a, st);
   }
 }
 

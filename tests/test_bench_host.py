@@ -49,7 +49,9 @@ def test_kernel_hash_ignores_comments_but_not_code(tmp_path):
     text = p.read_text()
     p.write_text("// a new comment line\n" + text.replace("\n", "\n\n", 3))
     assert bench.kernel_source_hash(str(copy)) == h0
-    p.write_text(text.replace("constexpr int RING = 2;", "constexpr int RING = 3;"))
+    code = "constexpr int B1_BLOCKS_PER_CU = 2;"
+    assert code in text
+    p.write_text(text.replace(code, "constexpr int B1_BLOCKS_PER_CU = 3;"))
     assert bench.kernel_source_hash(str(copy)) != h0
 
 
