@@ -136,6 +136,10 @@ bool generic_kernel(int fmt, int nb, int64_t hidden, int mode,
                     KernelDesc* out);
 // Largest batch slice the MFMA kernel can stage for this hidden size.
 int mfma_max_slice(int64_t hidden, int lds_per_block);
+// LDS the MFMA kernels declare statically (the finish's tables), kept out of
+// the h slice's budget; a CPU test checks the built kernels against it.
+constexpr int MFMA_STATIC_LDS = 4096;
+
 // LDS bytes of one staged h row in the MFMA kernel: whole 1 KB pieces plus
 // 16 bytes of bank skew.
 __host__ __device__ inline int mfma_lds_row_bytes(int64_t hidden) {

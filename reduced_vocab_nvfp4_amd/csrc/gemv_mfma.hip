@@ -429,14 +429,14 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
 }
 
 // Launch shape: one 16-row tile per unit, a double-buffered ring of slots,
-// one block per CU (the h slice fills most of the LDS).
-//   * NVFP4: 1024 threads (four waves per SIMD) and slots of four steps.
-//     Its decode makes each MFMA wait on a chain of converts, and more waves
-//     hide that latency (about 4% over 512 threads with ten-step slots on
-//     the 27B-shaped head, 1% on the 98K one).
-//   * E4M3 and BF16: 512 threads (two waves per SIMD, 256 VGPRs each for
-//     the ring) and slots of ten steps (ten 1 KB loads per slot).  This is
-//     2% faster than the NVFP4 shape on the 98K E4M3 head.
+// one block per CU (the h slice fills most of the LDS), 512 threads (two
+// waves per SIMD, 256 VGPRs each).
+//   * NVFP4: slots of four steps.  On the 98K head at batch 16 this is 7%
+//     faster than 1024 threads: the 6144 tiles then make three units for
+//     every wave instead of one and a half, and the extra waves bought no
+//     latency cover.
+//   * E4M3 and BF16: slots of ten steps (ten 1 KB loads per slot), 2%
+//     faster than the NVFP4 shape on the 98K E4M3 head.
 constexpr int MFMA_RT = 1;
 constexpr int MFMA_NB = 2;
 
@@ -447,7 +447,7 @@ struct MfmaShape {
 };
 template <>
 struct MfmaShape<Nvfp4> {
-  static constexpr int THREADS = 1024;
+  static constexpr int THREADS = 512;
   static constexpr int SPS = 4;
 };
 
@@ -520,7 +520,9 @@ bool pick(int64_t hidden, int nb, int mode, int lds_per_block,
 
 int mfma_max_slice(int64_t hidden, int lds_per_block) {
   const int64_t row = mfma_lds_row_bytes(hidden);
-  int64_t nb = (int64_t)lds_per_block / row - 1;
+  // the kernels' static LDS (the finish's tables) comes out of the same
+  // budget as the h slice
+  int64_t nb = ((int64_t)lds_per_block - MFMA_STATIC_LDS) / row - 1;
   if (nb > 16) nb = 16;
   return nb < 0 ? 0 : (int)nb;
 }

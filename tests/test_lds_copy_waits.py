@@ -14,6 +14,11 @@ for every kernel that copies into LDS, that the last vmcnt wait before its
 first LDS read is covered by vector loads issued, in straight-line code,
 after its last copy (the first such wait, which the kernels place before
 any LDS read).
+
+The same listings give each MFMA kernel's static LDS (the finish's tables),
+which the launch planner keeps out of the h slice's budget
+(MFMA_STATIC_LDS): a kernel that outgrew it could be planned a slice whose
+launch fails for want of LDS.
 """
 import concurrent.futures
 import glob
@@ -106,3 +111,15 @@ def test_lds_copy_waits_cover_the_copies(tmp_path):
                 checked += 1
     # the batch-1 kernels and the MFMA kernels of every format and mode
     assert checked >= 40, checked
+
+
+@pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="needs hipcc")
+def test_mfma_static_lds_within_the_reserve(tmp_path):
+    src = os.path.join(CSRC, "gemv_mfma.hip")
+    text = "\n".join(_asm(src, str(tmp_path / "mfma.s")))
+    with open(os.path.join(CSRC, "gemv_common.h")) as f:
+        reserve = int(re.search(r"MFMA_STATIC_LDS = (\d+);", f.read()).group(1))
+    sizes = [int(m.group(1)) for m in re.finditer(
+        r"\.amdhsa_group_segment_fixed_size (\d+)", text)]
+    assert len(sizes) >= 20, len(sizes)
+    assert max(sizes) <= reserve, (max(sizes), reserve)
