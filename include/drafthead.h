@@ -79,7 +79,7 @@ extern "C" {
 #define DH_EWORKSPACE (-2) /* workspace pointer null or too small */
 #define DH_EHIP (-3)       /* a HIP runtime call or kernel launch failed */
 
-#define DRAFTHEAD_ABI_VERSION 3
+#define DRAFTHEAD_ABI_VERSION 4
 
 /* Byte offsets of the two uint16 fields of a workspace a caller may read or
  * write (see "Give-up" above). */
@@ -163,6 +163,33 @@ int draft_head_top_tokens(const uint8_t* packed, const uint8_t* scales,
                           int64_t n_rows, int64_t hidden, const void* h_bf16,
                           int64_t batch, int32_t* out_ids, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * draft_head_top_tokens without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The finish state a
+ * workspace would carry lives in a static device array of the library
+ * (DRAFTHEAD_NOALLOC_SCRATCH_BYTES, the largest workspace any batch needs;
+ * each GPU holds its own copy until the process ends); the call allocates
+ * nothing.  Arguments, results and errors are those of
+ * draft_head_top_tokens, whose kernels it runs; a workspace size beyond the
+ * array, which no valid batch reaches, returns DH_EWORKSPACE.
+ * The array starts zeroed and carries the state from call to call as a
+ * workspace does, so nothing is cleared per call.  Every call on a GPU
+ * shares that GPU's array: calls that may overlap on one GPU (unordered
+ * streams, several host threads) race and must not be issued.  A give-up
+ * (see above) is sticky for the rest of the process on that GPU, since
+ * nothing can zero-fill the array again: draft_head_top_tokens with a
+ * workspace of the caller's remains available.
+ */
+#define DRAFTHEAD_NOALLOC_SCRATCH_BYTES 1048832
+int draft_head_top_tokens_noalloc(const uint8_t* packed,
+                                  const uint8_t* scales,
+                                  const float* global_scale,
+                                  const int32_t* dh_idx, int64_t n_rows,
+                                  int64_t hidden, const void* h_bf16,
+                                  int64_t batch, int32_t* out_ids,
+                                  void* stream);
 
 /*
  * Draft logits over the full vocabulary (page 1, compute_logits: the draft

@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.draft_head_top_tokens.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                             _c_i64, _c_i64, _c_ptr, _c_i64,
                                             _c_ptr, _c_ptr, _c_size, _c_ptr]
+        L.draft_head_top_tokens_noalloc.restype = ctypes.c_int
+        L.draft_head_top_tokens_noalloc.argtypes = [
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64,
+            _c_ptr, _c_ptr]
         L.draft_head_logits.restype = ctypes.c_int
         L.draft_head_logits.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_i64, _c_i64, _c_i64, _c_i64,
@@ -270,6 +274,26 @@ def draft_head_top_tokens(packed, scales, global_scale, dh_idx, h, *,
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(dev, stream))
     _check("draft_head_top_tokens", rc)
+    return out_ids
+
+
+def draft_head_top_tokens_noalloc(packed, scales, global_scale, dh_idx, h, *,
+                                  out_ids=None, stream=None):
+    """draft_head_top_tokens on the library's own static scratch (the C call
+    allocates nothing; calls that overlap on one GPU race): int32 [B] ids."""
+    n, H2 = packed.shape
+    B, H = h.shape
+    dev = h.device
+    if out_ids is None:
+        with _alloc_stream(stream):
+            out_ids = torch.empty(B, dtype=torch.int32, device=dev)
+    rc = lib().draft_head_top_tokens_noalloc(
+        _dev(packed, "packed", torch.uint8), _dev(scales, "scales", torch.uint8),
+        _dev(global_scale, "global_scale", torch.float32),
+        _dev(dh_idx, "dh_idx", torch.int32), n, H,
+        _dev(h, "h", torch.bfloat16), B,
+        _dev(out_ids, "out_ids", torch.int32), _stream(dev, stream))
+    _check("draft_head_top_tokens_noalloc", rc)
     return out_ids
 
 

@@ -75,6 +75,37 @@ static int check_head(int fmt, const void* w, const uint8_t* scales,
   return DH_OK;
 }
 
+// Scratch of draft_head_top_tokens_noalloc: the largest workspace any batch
+// needs, in static device storage (zero at load, one copy per GPU).  In host
+// code `scratch` names a host-side stand-in, not device memory: the address
+// kernels use is the one hipGetSymbolAddress returns with the device
+// current, fetched on a device's first call and kept per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES =
+    WS_SLOTS + (size_t)MAX_GRID * (size_t)MAX_SLICE * 16;
+static_assert(NOALLOC_SCRATCH_BYTES == DRAFTHEAD_NOALLOC_SCRATCH_BYTES,
+              "the header states the scratch size");
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+static hipError_t scratch_address(void** out) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEV];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 static int top_tokens(int fmt, const void* w, const uint8_t* scales,
                       const float* scale, const int32_t* dh_idx,
                       int64_t n_rows, int64_t hidden, const void* h,
@@ -333,6 +364,30 @@ int draft_head_top_tokens(const uint8_t* packed, const uint8_t* scales,
   return dh::top_tokens(dh::FMT_NVFP4, packed, scales, global_scale, dh_idx,
                         n_rows, hidden, h_bf16, batch, out_ids, workspace,
                         workspace_bytes, stream);
+}
+
+int draft_head_top_tokens_noalloc(const uint8_t* packed,
+                                  const uint8_t* scales,
+                                  const float* global_scale,
+                                  const int32_t* dh_idx, int64_t n_rows,
+                                  int64_t hidden, const void* h_bf16,
+                                  int64_t batch, int32_t* out_ids,
+                                  void* stream) {
+  // every argument error is reported before the first HIP call: the checks
+  // run against an aligned stand-in for the scratch's address
+  const size_t need = dh::workspace_bytes(n_rows, batch);
+  if (need > dh::NOALLOC_SCRATCH_BYTES) return DH_EWORKSPACE;
+  if (!out_ids || !dh::aligned(out_ids, 4)) return DH_EINVAL;
+  int rc = dh::check_head(dh::FMT_NVFP4, packed, scales, global_scale, dh_idx,
+                          n_rows, hidden, h_bf16, batch,
+                          reinterpret_cast<void*>(uintptr_t{256}),
+                          dh::NOALLOC_SCRATCH_BYTES);
+  if (rc != DH_OK) return rc;
+  void* ws = nullptr;
+  if (dh::scratch_address(&ws) != hipSuccess) return DH_EHIP;
+  return dh::top_tokens(dh::FMT_NVFP4, packed, scales, global_scale, dh_idx,
+                        n_rows, hidden, h_bf16, batch, out_ids, ws,
+                        dh::NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int draft_head_logits(const uint8_t* packed, const uint8_t* scales,

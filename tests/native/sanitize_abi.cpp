@@ -48,6 +48,22 @@ extern "C" hipError_t hipGetDevice(int* d) {
   *d = 0;
   return hipSuccess;
 }
+// api.hip holds one static device array (the scratch of the no-allocation
+// entry point): its registration at load and the address query are stubbed
+// too; the address is a fake aligned pointer, never dereferenced.
+static int symbol_queries = 0;
+extern "C" void** __hipRegisterFatBinary(const void*) {
+  static void* handle = nullptr;
+  return &handle;
+}
+extern "C" void __hipUnregisterFatBinary(void**) {}
+extern "C" void __hipRegisterVar(void**, void*, char*, char*, int, size_t,
+                                 int, int) {}
+extern "C" hipError_t hipGetSymbolAddress(void** p, const void*) {
+  *p = reinterpret_cast<void*>(uintptr_t(3) << 40);
+  ++symbol_queries;
+  return hipSuccess;
+}
 extern "C" hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t,
                                             int) {
   *v = 256;
@@ -173,6 +189,24 @@ int main() {
   LAUNCHED(draft_head_top_tokens(P8, P8, PF, PI, N, H, P, 16, PI, P, ws16,
                                  nullptr),
            1);
+  // the scratch address is queried once per device, then kept
+  LAUNCHED(draft_head_top_tokens_noalloc(P8, P8, PF, PI, N, H, P, 1, PI,
+                                         nullptr),
+           1);
+  LAUNCHED(draft_head_top_tokens_noalloc(P8, P8, PF, PI, N, H, P, 64, PI,
+                                         nullptr),
+           1);
+  EXPECT(symbol_queries == 1);
+  REFUSED(draft_head_top_tokens_noalloc(nullptr, P8, PF, PI, N, H, P, 1, PI,
+                                        nullptr),
+          DH_EINVAL);
+  REFUSED(draft_head_top_tokens_noalloc(P8, P8, PF, PI, N, H, P, 65, PI,
+                                        nullptr),
+          DH_EINVAL);
+  REFUSED(draft_head_top_tokens_noalloc(P8, P8, PF, PI, N, H, P, 1,
+                                        reinterpret_cast<int32_t*>(MIS),
+                                        nullptr),
+          DH_EINVAL);
   LAUNCHED(draft_head_top_tokens_compat(P8, P8, PF, PI, N, H, P, 3, PI, P,
                                         ws16, nullptr),
            1);

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(dh.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared but not exported"
-    assert dh.lib().drafthead_abi_version() == 3
+    assert dh.lib().drafthead_abi_version() == 4
     assert dh.error_string(dh.DH_EINVAL).startswith("invalid")
 
 
@@ -130,6 +130,35 @@ def test_top_tokens_and_logits_reject_bad_arguments_on_the_host():
     assert logits(n_kept=129) == dh.DH_EINVAL
     assert logits(vocab=50) == dh.DH_EINVAL
     assert logits(out=FAKE + 4) == dh.DH_EINVAL
+
+
+def test_noalloc_top_tokens_rejects_bad_arguments_on_the_host():
+    """The entry point without a workspace checks every argument before its
+    first HIP call (the scratch address is fetched only after them)."""
+    L = dh.lib()
+    base = dict(p=FAKE, s=FAKE, g=FAKE, idx=FAKE, n=128, H=256, h=FAKE, B=1,
+                out=FAKE)
+
+    def top(**kw):
+        a = {**base, **kw}
+        return L.draft_head_top_tokens_noalloc(
+            a["p"], a["s"], a["g"], a["idx"], a["n"], a["H"], a["h"], a["B"],
+            a["out"], None)
+    assert top(p=None) == dh.DH_EINVAL
+    assert top(s=None) == dh.DH_EINVAL
+    assert top(g=None) == dh.DH_EINVAL
+    assert top(idx=None) == dh.DH_EINVAL
+    assert top(h=None) == dh.DH_EINVAL
+    assert top(out=None) == dh.DH_EINVAL
+    assert top(out=FAKE + 2) == dh.DH_EINVAL
+    assert top(n=100) == dh.DH_EINVAL
+    assert top(H=40) == dh.DH_EINVAL
+    assert top(B=0) == dh.DH_EINVAL
+    assert top(B=65) == dh.DH_EINVAL     # beyond the largest batch
+    assert top(p=FAKE + 8) == dh.DH_EINVAL
+    # the largest workspace any batch needs is the scratch's size
+    assert (dh.draft_head_workspace_bytes(1 << 20, 64)
+            <= 1048832 == dh.draft_head_workspace_bytes(128, 64))
 
 
 def test_e4m3_quantize_rejects_bad_arguments_on_the_host():

@@ -3,10 +3,11 @@
 * The oracle (oracle/oracle.c), built with gcc and -fsanitize=address,
   undefined, driven through every entry point on small heads and edge-case
   masks by tests/native/sanitize_oracle.c.
-* The C-ABI layer (csrc/api.hip) compiled for the host only with the same
-  sanitizers (hipcc, host flags only), linked with tests/native/
-  sanitize_abi.cpp, which stubs the kernel launchers and the two HIP
-  queries and calls every entry point with refused and accepted arguments.
+* The C-ABI layer (csrc/api.hip) compiled with the same sanitizers on its
+  host side (hipcc, host flags only), linked with tests/native/
+  sanitize_abi.cpp, which stubs the kernel launchers, the HIP queries and
+  the registration of api.hip's one device array, and calls every entry
+  point with refused and accepted arguments.
 
 Either run fails on the first sanitizer report (no recovery) or on a wrong
 return code.
@@ -47,17 +48,21 @@ def test_oracle_under_address_and_undefined_sanitizers(tmp_path):
 def test_c_abi_host_layer_under_address_and_undefined_sanitizers(tmp_path):
     inc = ["-I", os.path.join(ROOT, "include"), "-I",
            os.path.join(ROOT, "reduced_vocab_nvfp4_amd", "csrc")]
-    flags = ["-x", "hip", "--offload-host-only", "-O1", "-g", "-std=c++17",
+    flags = ["-x", "hip", "-O1", "-g", "-std=c++17",
              "-fno-omit-frame-pointer",
              "-Xarch_host", "-fsanitize=address",
              "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-sanitize-recover=all"]
     objs = []
-    for src in (os.path.join(ROOT, "reduced_vocab_nvfp4_amd", "csrc",
-                             "api.hip"),
-                os.path.join(NATIVE, "sanitize_abi.cpp")):
+    # api.hip declares a device array, so it is built with its device code
+    # (the sanitizers apply to the host side only); the driver is host code
+    for src, target in (
+            (os.path.join(ROOT, "reduced_vocab_nvfp4_amd", "csrc", "api.hip"),
+             ["--offload-arch=gfx950"]),
+            (os.path.join(NATIVE, "sanitize_abi.cpp"),
+             ["--offload-host-only"])):
         obj = str(tmp_path / (os.path.basename(src) + ".o"))
-        _run([HIPCC, *flags, *inc, "-c", src, "-o", obj])
+        _run([HIPCC, *target, *flags, *inc, "-c", src, "-o", obj])
         objs.append(obj)
     exe = str(tmp_path / "sanitize_abi")
     _run([CLANGXX, "-fsanitize=address,undefined", *objs, "-o", exe])
