@@ -105,12 +105,13 @@ struct Nvfp4 {
   }
 
   // MFMA operand T (elements 8T .. 8T+7 of the chunk, all in block T/2):
-  // the dequantized weights e2m1 * e4m3 as eight BF16.
-  template <int T>
+  // the dequantized weights e2m1 * e4m3 as eight BF16.  The chunk's two
+  // scale bytes are bytes SB and SB + 1 of sb.
+  template <int T, int SB = 0>
   __device__ static __forceinline__ bf16x8 operand(const uint4& p,
                                                    uint32_t sb) {
     const uint32_t w = T == 0 ? p.x : T == 1 ? p.y : T == 2 ? p.z : p.w;
-    const float s = __builtin_amdgcn_cvt_f32_fp8(sb, T / 2);
+    const float s = __builtin_amdgcn_cvt_f32_fp8(sb, SB + T / 2);
     const uint4 r = make_uint4(fp4_scaled_pair<0>(w, s), fp4_scaled_pair<1>(w, s),
                                fp4_scaled_pair<2>(w, s), fp4_scaled_pair<3>(w, s));
     return __builtin_bit_cast(bf16x8, r);
@@ -152,7 +153,7 @@ struct E4m3 {
     return fp8_dot4(p.y, hp + 2, fp8_dot4(p.x, hp, acc));
   }
 
-  template <int T>
+  template <int T, int SB = 0>
   __device__ static __forceinline__ bf16x8 operand(const uint4& p, uint32_t) {
     const uint32_t w0 = T == 0 ? p.x : p.z, w1 = T == 0 ? p.y : p.w;
     const uint4 r = make_uint4(fp8_pair<false>(w0), fp8_pair<true>(w0),
@@ -184,7 +185,7 @@ struct Bf16 {
     return dot2(p.y, hp[1], dot2(p.x, hp[0], acc));
   }
 
-  template <int T>
+  template <int T, int SB = 0>
   __device__ static __forceinline__ bf16x8 operand(const uint4& p, uint32_t) {
     return __builtin_bit_cast(bf16x8, p);
   }

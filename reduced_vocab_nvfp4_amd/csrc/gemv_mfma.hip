@@ -38,26 +38,78 @@ namespace {
 // is read SPS*64 contiguous bytes at a time.
 //
 // Block scales (NVFP4): step c of a slot needs the two scale bytes of chunk
-// 4c + q, 8 bytes apart from step to step.  With an even SPS the slot's
-// 8*SPS scale bytes of the lane's row are loaded as SPS/2 16-byte pieces
-// (the four lanes of a row load the same pieces) and each step picks its two
-// bytes out of them; an odd SPS loads them as one 16-bit value per step.
+// 4c + q, 8 bytes apart from step to step.
+//   * Four steps per slot (the NVFP4 shape): the slot's 32 scale bytes of a
+//     row are 4 x 4 pairs, pair (c, q) at byte 8c + 2q.  Lane (n, q) loads
+//     the 8 bytes 8q .. 8q+7, which are step q's pairs of the row's four
+//     lanes, and a transpose over the wave's four 16-lane rows
+//     (transpose_scale_pairs) hands each lane its own pairs of steps 0..3.
+//     One 8-byte load per lane per slot, no byte loaded twice.
+//   * Another even SPS: the slot's 8*SPS scale bytes of the lane's row are
+//     loaded as SPS/2 16-byte pieces (the four lanes of a row load the same
+//     pieces) and each step picks its two bytes out of them.
+//   * An odd SPS loads them as one 16-bit value per step.
+template <class F, int SPS>
+constexpr bool pair_scales() {
+  return F::SCALED && SPS == 4;
+}
 template <class F, int SPS>
 constexpr bool wide_scales() {
-  return F::SCALED && SPS % 2 == 0;
+  return F::SCALED && SPS % 2 == 0 && !pair_scales<F, SPS>();
 }
 
 template <class F, int RT, int SPS>
 struct Slot {
   uint4 p[RT][SPS];
-  uint32_t s[RT][wide_scales<F, SPS>() ? 1 : SPS];
+  uint32_t s[RT][F::SCALED && SPS % 2 == 1 ? SPS : 1];
   uint4 sw[RT][wide_scales<F, SPS>() ? SPS / 2 : 1];
+  uint2 sp[RT];  // pair_scales: the lane's 8 bytes, as loaded
   // scatter modes: lane l holds dh_idx[r0 - 1 + min(l, 16)] of tile t (r0
   // its first row; row -1 reads row 0): the kept id before the tile, then
   // the tile's 16 ids.  The address depends on the lane, so this is a
   // vector load, which the prologue's wait count relies on.
   int32_t ids[RT];
 };
+
+// pair_scales: lane (n, q) holds v, bytes 8q .. 8q+7 of the slot's 32 scale
+// bytes of head row n, which are pairs (q, 0..3), pair (c, r) being the two
+// scale bytes of chunk 4c + r.  Returns pairs (0..3, q), the lane's own
+// pairs of steps 0..3 (step c in half c%2 of word c/2): a 4x4 transpose of
+// 16-bit values over the wave's four 16-lane rows.
+//   1. v_permlane32_swap trades word 1 of rows 0, 1 for word 0 of rows 2, 3.
+//      Rows 0, 1 then hold pairs (q, 0..1) in a and (q+2, 0..1) in b, rows
+//      2, 3 pairs (q-2, 2..3) in a and (q, 2..3) in b.
+//   2. In each row pair (0, 1) and (2, 3) the even row sends the high
+//      halves of a and b and keeps the low ones, the odd row the reverse
+//      (v_perm_b32 with the lane's selector sel.s); v_permlane16_swap trades
+//      the sent words between the two rows, and two more v_perm_b32 put the
+//      kept and the received halves in step order.
+struct PairSel {
+  uint32_t s, y0, y1;  // byte selectors of v_perm_b32 for this lane's row
+  bool odd;            // the lane's row q is odd
+};
+
+__device__ __forceinline__ PairSel pair_selectors(int q) {
+  const bool odd = (q & 1) != 0;
+  // v_perm_b32(hi, lo, sel): selector byte i picks byte i of the result,
+  // 0-3 from lo, 4-7 from hi
+  return odd ? PairSel{0x05040100u, 0x03020504u, 0x03020706u, true}
+             : PairSel{0x07060302u, 0x05040100u, 0x07060100u, false};
+}
+
+__device__ __forceinline__ uint2 transpose_scale_pairs(uint2 v,
+                                                       const PairSel& sel) {
+  const auto w = __builtin_amdgcn_permlane32_swap(v.x, v.y, false, false);
+  const uint32_t a = w[0], b = w[1];
+  const uint32_t s = __builtin_amdgcn_perm(b, a, sel.s);
+  // odd rows of the first operand trade with even rows of the second: an
+  // even row finds its partner's word in the second result, an odd row in
+  // the first
+  const auto x = __builtin_amdgcn_permlane16_swap(s, s, false, false);
+  const uint32_t r = sel.odd ? x[0] : x[1];
+  return make_uint2(__builtin_amdgcn_perm(r, a, sel.y0),
+                    __builtin_amdgcn_perm(r, b, sel.y1));
+}
 
 // The two scale bytes of step C for a lane of k-slot group q.
 template <class F, int RT, int SPS, int C>
@@ -79,8 +131,9 @@ __device__ __forceinline__ uint32_t slot_scale(const Slot<F, RT, SPS>& b,
 }
 
 // The EPC/8 MFMAs of one step: operand O of every tile's chunk against the
-// h slots O of the lane's chunk.
-template <class F, int O, int RT, int SPS>
+// h slots O of the lane's chunk.  The chunk's scale bytes are bytes SB and
+// SB + 1 of sc[t].
+template <class F, int O, int RT, int SPS, int SB>
 __device__ __forceinline__ void mfma_ops(const Slot<F, RT, SPS>& b, int c,
                                          const uint32_t (&sc)[RT],
                                          const char* hp, f32x4 (&acc)[RT]) {
@@ -89,21 +142,29 @@ __device__ __forceinline__ void mfma_ops(const Slot<F, RT, SPS>& b, int c,
 #pragma unroll
     for (int t = 0; t < RT; ++t)
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          av, F::template operand<O>(b.p[t][c], sc[t]), acc[t], 0, 0, 0);
-    mfma_ops<F, O + 1, RT, SPS>(b, c, sc, hp, acc);
+          av, F::template operand<O, SB>(b.p[t][c], sc[t]), acc[t], 0, 0, 0);
+    mfma_ops<F, O + 1, RT, SPS, SB>(b, c, sc, hp, acc);
   }
 }
 
-// The SPS steps of one slot.
+// The SPS steps of one slot (pr: the transposed scale pairs, pair_scales).
 template <class F, int C, int RT, int SPS>
-__device__ __forceinline__ void slot_steps(const Slot<F, RT, SPS>& b, int q,
+__device__ __forceinline__ void slot_steps(const Slot<F, RT, SPS>& b,
+                                           const uint2 (&pr)[RT], int q,
                                            const char* hp, f32x4 (&acc)[RT]) {
   if constexpr (C < SPS) {
     uint32_t sc[RT];
+    const char* hc = hp + C * (4 * F::EPC * 2);
+    if constexpr (pair_scales<F, SPS>()) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) sc[t] = slot_scale<F, RT, SPS, C>(b, t, q);
-    mfma_ops<F, 0, RT, SPS>(b, C, sc, hp + C * (4 * F::EPC * 2), acc);
-    slot_steps<F, C + 1, RT, SPS>(b, q, hp, acc);
+      for (int t = 0; t < RT; ++t) sc[t] = C < 2 ? pr[t].x : pr[t].y;
+      mfma_ops<F, 0, RT, SPS, 2 * (C % 2)>(b, C, sc, hc, acc);
+    } else {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) sc[t] = slot_scale<F, RT, SPS, C>(b, t, q);
+      mfma_ops<F, 0, RT, SPS, 0>(b, C, sc, hc, acc);
+    }
+    slot_steps<F, C + 1, RT, SPS>(b, pr, q, hp, acc);
   }
 }
 
@@ -199,8 +260,11 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   for (int t = 0; t < RT; ++t) {
     woff[t] = (uint32_t)((16 * t + n) * RB + q * 16);
     soff[t] = (uint32_t)((16 * t + n) * SPR +
-                         (wide_scales<F, SPS>() ? 0 : q * 2));
+                         (wide_scales<F, SPS>()   ? 0
+                          : pair_scales<F, SPS>() ? q * 8
+                                                  : q * 2));
   }
+  const PairSel psel = pair_selectors(q);
   // A-operand LDS address of this lane at step 0: batch row min(m, nb)
   // (row nb is zero), chunk q.
   const int mrow = n < nb ? n : nb;
@@ -219,13 +283,20 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
     int js = ld_js;
     asm volatile("" : "+s"(row0), "+s"(js));
     const uint8_t* wb = a.w + row0 * RB + (int64_t)js * (64 * SPS);
+    const uint8_t* sb = a.scales + row0 * SPR + (int64_t)js * (8 * SPS);
+    // pair scales first: the transpose needs only them, so it can run while
+    // the slot's code loads are still arriving
+    if constexpr (pair_scales<F, SPS>()) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        b.sp[t] = *reinterpret_cast<const uint2*>(sb + soff[t]);
+    }
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
       for (int c = 0; c < SPS; ++c)
         b.p[t][c] = *reinterpret_cast<const uint4*>(wb + woff[t] + 64 * c);
-    if constexpr (F::SCALED) {
-      const uint8_t* sb = a.scales + row0 * SPR + (int64_t)js * (8 * SPS);
+    if constexpr (F::SCALED && !pair_scales<F, SPS>()) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -323,8 +394,10 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   Slot<F, RT, SPS> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB - 1; ++k) load(buf[k]);
-  constexpr int SCALE_LOADS =
-      wide_scales<F, SPS>() ? SPS / 2 : (F::SCALED ? SPS : 0);
+  constexpr int SCALE_LOADS = pair_scales<F, SPS>()   ? 1
+                              : wide_scales<F, SPS>() ? SPS / 2
+                              : F::SCALED             ? SPS
+                                                      : 0;
   constexpr int WEIGHT_LOADS =
       (NB - 1) * (RT * (SPS + SCALE_LOADS) + (is_scatter(MODE) ? RT : 0));
   static_assert(WEIGHT_LOADS <= 63, "vmcnt field is 6 bits");
@@ -342,8 +415,13 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if (s0 + k < n_s) {  // wave-uniform
         const Slot<F, RT, SPS>& b = buf[k];
+        uint2 pr[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          pr[t] = pair_scales<F, SPS>() ? transpose_scale_pairs(b.sp[t], psel)
+                                        : make_uint2(0u, 0u);
         slot_steps<F, 0, RT, SPS>(
-            b, q, hsb + hoff + cp_js * SPS * (4 * F::EPC * 2), acc);
+            b, pr, q, hsb + hoff + cp_js * SPS * (4 * F::EPC * 2), acc);
         if (cp_js == js1 - 1) {
           // unit done: rows row0 + 16t + n, batch rows 4q + j (a split
           // unit's parts are added after the loop)
