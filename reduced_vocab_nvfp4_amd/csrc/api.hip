@@ -192,10 +192,11 @@ static int quantize_nvfp4(const void* w, bool f16, int64_t vocab,
 // W8A8 workspace: the argmax state of any top-token call (the slots of the
 // widest batch, so a workspace shared with other calls never overlaps
 // them), then the tokens' activations (the BF16 values of their E4M3 codes,
-// [batch][hidden]) and their scales, scratch that each call rewrites before
-// reading.  total == 0 for an invalid shape.
+// [batch][hidden]), their codes ([batch][hidden] bytes) and their scales,
+// scratch that each call rewrites before reading.  total == 0 for an
+// invalid shape.
 struct W8a8Layout {
-  size_t act, sx, total;
+  size_t act, codes, sx, total;
 };
 
 static W8a8Layout w8a8_layout(int64_t n_rows, int64_t batch, int64_t hidden) {
@@ -205,16 +206,19 @@ static W8a8Layout w8a8_layout(int64_t n_rows, int64_t batch, int64_t hidden) {
     return l;
   const size_t state = workspace_bytes(n_rows, MAX_BATCH);
   l.act = (state + 255) / 256 * 256;
-  l.sx = l.act + ((size_t)batch * (size_t)hidden * 2 + 255) / 256 * 256;
+  l.codes = l.act + ((size_t)batch * (size_t)hidden * 2 + 255) / 256 * 256;
+  l.sx = l.codes + ((size_t)batch * (size_t)hidden + 255) / 256 * 256;
   l.total = l.sx + ((size_t)batch * 4 + 255) / 256 * 256;
   return l;
 }
 
 // The FP8 head's step: per-token E4M3 quantization of h into the
-// workspace, then the E4M3 GEMV on the tokens' exact BF16 values (each
-// product is a product of two E4M3 values, as in an FP8 GEMM).  The logits
-// carry each token's scale; the top token does not need it (a positive
-// factor per batch row leaves the row's argmax unchanged).
+// workspace (codes and their exact BF16 values), then the E4M3 GEMV: the
+// batched slices multiply the codes with the head's bytes on the FP8 matrix
+// cores, a batch-1 slice (a stream kernel) uses the BF16 values; either way
+// each product is a product of two E4M3 values, as in an FP8 GEMM.  The
+// logits carry each token's scale; the top token does not need it (a
+// positive factor per batch row leaves the row's argmax unchanged).
 static int w8a8(const uint8_t* q, const float* scale, const int32_t* dh_idx,
                 int64_t n_rows, int64_t n_kept, int64_t hidden, int64_t vocab,
                 const void* h, int64_t batch, int32_t* out_ids, float* out,
@@ -233,10 +237,11 @@ static int w8a8(const uint8_t* q, const float* scale, const int32_t* dh_idx,
   if (ws_bytes < l.total) return DH_EWORKSPACE;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   uint16_t* hq = reinterpret_cast<uint16_t*>(wsb + l.act);
+  uint8_t* qx = wsb + l.codes;
   float* sx = reinterpret_cast<float*>(wsb + l.sx);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = launch_fp8_tokens(static_cast<const uint16_t*>(h),
-                                         batch, hidden, nullptr, hq, sx, s);
+                                         batch, hidden, qx, hq, sx, s);
   if (e != hipSuccess) return DH_EHIP;
   GemvArgs a{};
   a.fmt = FMT_E4M3;
@@ -246,6 +251,7 @@ static int w8a8(const uint8_t* q, const float* scale, const int32_t* dh_idx,
   a.n_rows = n_rows;
   a.hidden = hidden;
   a.h = hq;
+  a.h_fp8 = qx;
   a.batch = batch;
   a.ws = wsb;
   if (out_ids) {

@@ -93,6 +93,10 @@ struct GemvArgs {
   // Logits only: one more factor per batch row (the W8A8 head's token
   // scales), null for none.
   const float* row_scale = nullptr;
+  // The W8A8 step (E4M3 head): the tokens' E4M3 codes [batch][hidden]
+  // beside their BF16 values in h; the batched slices multiply the codes on
+  // the FP8 matrix cores, the others use h.  Null otherwise.
+  const uint8_t* h_fp8 = nullptr;
   // The pages' own numerics (NVFP4 only): the top token of the scaled
   // logits rounded to BF16, or BF16 logits (out_logits then points to
   // BF16 [batch][vocab]).

@@ -81,6 +81,7 @@ struct Nvfp4 {
   static constexpr int EPC = 32;  // elements per 16-byte chunk
   static constexpr int EPU = 16;  // elements per 8-byte unit (one block)
   static constexpr bool SCALED = true;
+  static constexpr bool FP8_ACT = false;  // h is BF16
 
   // One chunk (two 16-element blocks; their E4M3 scales in bytes 0/1 of sb)
   // against EPC/2 = 16 BF16 pairs of h.
@@ -137,6 +138,7 @@ struct E4m3 {
   static constexpr int EPC = 16;
   static constexpr int EPU = 8;
   static constexpr bool SCALED = false;
+  static constexpr bool FP8_ACT = false;  // h is BF16
 
   __device__ static __forceinline__ float chunk_dot(const uint4& p, uint32_t,
                                                     const uint32_t* hp,
@@ -162,6 +164,24 @@ struct E4m3 {
   }
 };
 
+// The same E4M3 head against E4M3 activation codes (the W8A8 step): both
+// MFMA operands are raw E4M3 bytes (v_mfma_f32_16x16x32_fp8_fp8), so the
+// weights need no decode at all; h is staged as the tokens' codes, one byte
+// per element.  The products of two E4M3 values are exact in fp32.
+struct E4m3Fp8 {
+  static constexpr int kFmt = FMT_E4M3;
+  static constexpr int EPC = 16;
+  static constexpr int EPU = 8;
+  static constexpr bool SCALED = false;
+  static constexpr bool FP8_ACT = true;
+
+  // MFMA operand T: bytes 8T .. 8T+7 of the chunk, as they are
+  template <int T>
+  __device__ static __forceinline__ uint64_t operand8(const uint4& p) {
+    return T == 0 ? ((uint64_t)p.y << 32 | p.x) : ((uint64_t)p.w << 32 | p.z);
+  }
+};
+
 // ------------------------------------------------------------------- BF16
 
 struct Bf16 {
@@ -169,6 +189,7 @@ struct Bf16 {
   static constexpr int EPC = 8;
   static constexpr int EPU = 4;
   static constexpr bool SCALED = false;
+  static constexpr bool FP8_ACT = false;  // h is BF16
 
   __device__ static __forceinline__ float chunk_dot(const uint4& p, uint32_t,
                                                     const uint32_t* hp,

@@ -125,25 +125,28 @@ struct KernelDesc {
   int split_slots;    // > 0: the waves of a block may split a unit's
                       // split_slots slots over the hidden dimension
   int per_cu;         // > 0: blocks per CU to launch (else as many as fit)
+  bool fp8_act = false;  // reads h as E4M3 codes (GemvArgs::h_fp8)
 };
 
 // Kernel families; each returns false when it has no kernel for the shape.
 // mode is an OutMode; the dense mode exists for NVFP4 only.
 bool b1_kernel(int fmt, int64_t hidden, int mode, KernelDesc* out);
+// fp8_act: h holds E4M3 codes (the W8A8 step), one byte per element.
 bool mfma_kernel(int fmt, int64_t hidden, int nb, int mode,
-                 int lds_per_block, KernelDesc* out);
+                 int lds_per_block, bool fp8_act, KernelDesc* out);
 bool generic_kernel(int fmt, int nb, int64_t hidden, int mode,
                     KernelDesc* out);
 // Largest batch slice the MFMA kernel can stage for this hidden size.
-int mfma_max_slice(int64_t hidden, int lds_per_block);
+int mfma_max_slice(int64_t hidden, int lds_per_block, int h_bytes = 2);
 // LDS the MFMA kernels declare statically (the finish's tables), kept out of
 // the h slice's budget; a CPU test checks the built kernels against it.
 constexpr int MFMA_STATIC_LDS = 4096;
 
 // LDS bytes of one staged h row in the MFMA kernel: whole 1 KB pieces plus
 // 16 bytes of bank skew.
-__host__ __device__ inline int mfma_lds_row_bytes(int64_t hidden) {
-  return (int)((hidden * 2 + 1023) / 1024 * 1024 + 16);
+__host__ __device__ inline int mfma_lds_row_bytes(int64_t hidden,
+                                                  int h_bytes = 2) {
+  return (int)((hidden * h_bytes + 1023) / 1024 * 1024 + 16);
 }
 
 __device__ __forceinline__ uint64_t pack_partial(float v, int r) {

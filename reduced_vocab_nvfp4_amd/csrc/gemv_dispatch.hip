@@ -88,10 +88,11 @@ hipError_t plan_slice(const GemvArgs& ga, int64_t remaining,
     return hipSuccess;
   }
   if (remaining >= 2) {
-    int nb = mfma_max_slice(ga.hidden, di.lds_per_block);
+    const bool fp8 = ga.h_fp8 != nullptr;
+    int nb = mfma_max_slice(ga.hidden, di.lds_per_block, fp8 ? 1 : 2);
     if (nb > remaining) nb = (int)remaining;
-    if (nb >= 2 &&
-        mfma_kernel(ga.fmt, ga.hidden, nb, mode, di.lds_per_block, d)) {
+    if (nb >= 2 && mfma_kernel(ga.fmt, ga.hidden, nb, mode, di.lds_per_block,
+                               fp8, d)) {
       *bc = nb;
       return hipSuccess;
     }
@@ -145,7 +146,9 @@ hipError_t launch_gemv(const GemvArgs& ga, hipStream_t s) {
     k.dh_idx = ga.dense ? nullptr : ga.dh_idx;
     k.n_rows = ga.n_rows;
     k.hidden = ga.hidden;
-    k.h = ga.h + b0 * ga.hidden;
+    // the W8A8 step's FP8 kernel reads the codes, every other kernel h
+    k.h = d.fp8_act ? reinterpret_cast<const uint16_t*>(ga.h_fp8 + b0 * ga.hidden)
+                    : ga.h + b0 * ga.hidden;
     k.nb = bc;
     k.out_ids = logits ? nullptr : ga.out_ids + b0;
     // dense: every row is written, out has n_rows columns

@@ -130,6 +130,12 @@ __device__ __forceinline__ uint32_t slot_scale(const Slot<F, RT, SPS>& b,
   }
 }
 
+// Bytes of one staged h element: BF16, or an E4M3 code (W8A8).
+template <class F>
+constexpr int h_elem_bytes() {
+  return F::FP8_ACT ? 1 : 2;
+}
+
 // The EPC/8 MFMAs of one step: operand O of every tile's chunk against the
 // h slots O of the lane's chunk.  The chunk's scale bytes are bytes SB and
 // SB + 1 of sc[t].
@@ -138,11 +144,22 @@ __device__ __forceinline__ void mfma_ops(const Slot<F, RT, SPS>& b, int c,
                                          const uint32_t (&sc)[RT],
                                          const char* hp, f32x4 (&acc)[RT]) {
   if constexpr (O < F::EPC / 8) {
-    const bf16x8 av = *reinterpret_cast<const bf16x8*>(hp + 16 * O);
+    if constexpr (F::FP8_ACT) {
+      // eight E4M3 codes of h against eight E4M3 weights
+      const uint64_t av = *reinterpret_cast<const uint64_t*>(hp + 8 * O);
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          av, F::template operand<O, SB>(b.p[t][c], sc[t]), acc[t], 0, 0, 0);
+      for (int t = 0; t < RT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+            (long)av, (long)F::template operand8<O>(b.p[t][c]), acc[t], 0, 0,
+            0);
+    } else {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(hp + 16 * O);
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            av, F::template operand<O, SB>(b.p[t][c], sc[t]), acc[t], 0, 0,
+            0);
+    }
     mfma_ops<F, O + 1, RT, SPS, SB>(b, c, sc, hp, acc);
   }
 }
@@ -154,7 +171,7 @@ __device__ __forceinline__ void slot_steps(const Slot<F, RT, SPS>& b,
                                            const char* hp, f32x4 (&acc)[RT]) {
   if constexpr (C < SPS) {
     uint32_t sc[RT];
-    const char* hc = hp + C * (4 * F::EPC * 2);
+    const char* hc = hp + C * (4 * F::EPC * h_elem_bytes<F>());
     if constexpr (pair_scales<F, SPS>()) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) sc[t] = C < 2 ? pr[t].x : pr[t].y;
@@ -229,9 +246,10 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   // h [nb][hidden] and one zero row are staged in LDS; a row takes whole
   // 1 KB pieces plus 16 bytes (SB bytes), so the 16 batch rows of an A-operand
   // read fall on different banks.
-  const int RBH = (int)(hidden * 2);  // h bytes per row
+  constexpr int HB = h_elem_bytes<F>();
+  const int RBH = (int)(hidden * HB);  // h bytes per row
   const int PPR = (RBH + 1023) / 1024;
-  const int SB = mfma_lds_row_bytes(hidden);
+  const int SB = mfma_lds_row_bytes(hidden, HB);
 
   // Units are dealt to groups of ks waves, group-major (unit u goes to group
   // u / gridDim.x of block u % gridDim.x), so every block gets work even when
@@ -268,7 +286,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
   // A-operand LDS address of this lane at step 0: batch row min(m, nb)
   // (row nb is zero), chunk q.
   const int mrow = n < nb ? n : nb;
-  const uint32_t hoff = (uint32_t)(mrow * SB + q * F::EPC * 2);
+  const uint32_t hoff = (uint32_t)(mrow * SB + q * F::EPC * HB);
   const char* hsb = reinterpret_cast<const char*>(hs);
 
   // Scalar cursor over (unit, slot) pairs: first row of the unit, slot.
@@ -421,7 +439,7 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
           pr[t] = pair_scales<F, SPS>() ? transpose_scale_pairs(b.sp[t], psel)
                                         : make_uint2(0u, 0u);
         slot_steps<F, 0, RT, SPS>(
-            b, pr, q, hsb + hoff + cp_js * SPS * (4 * F::EPC * 2), acc);
+            b, pr, q, hsb + hoff + cp_js * SPS * (4 * F::EPC * HB), acc);
         if (cp_js == js1 - 1) {
           // unit done: rows row0 + 16t + n, batch rows 4q + j (a split
           // unit's parts are added after the loop)
@@ -533,9 +551,12 @@ struct MfmaShape<Nvfp4> {
 template <class F, int SPS, int L>
 KernelDesc desc(int64_t steps) {
   constexpr int NT = MfmaShape<F>::THREADS;
+  // one block per CU: the units are dealt over the grid's waves, and a
+  // second block (which fits when h is staged as one-byte codes) would
+  // leave the waves of the 98K head with one and a half units each
   return KernelDesc{
       reinterpret_cast<const void*>(k_mfma<F, MFMA_RT, SPS, MFMA_NB, L, NT>),
-      NT, 16 * MFMA_RT, 0, true, L == OUT_DENSE ? (int)(steps / SPS) : 0};
+      NT, 16 * MFMA_RT, 0, true, L == OUT_DENSE ? (int)(steps / SPS) : 0, 1};
 }
 
 // Steps per slot: the format's preferred size if it divides the steps of a
@@ -567,8 +588,9 @@ KernelDesc desc_mode(bool one_step, int64_t steps) {
 template <class F>
 bool pick(int64_t hidden, int nb, int mode, int lds_per_block,
           KernelDesc* d) {
+  constexpr int HB = h_elem_bytes<F>();
   if (hidden % (4 * F::EPC) != 0) return false;
-  if (nb < 1 || nb > mfma_max_slice(hidden, lds_per_block)) return false;
+  if (nb < 1 || nb > mfma_max_slice(hidden, lds_per_block, HB)) return false;
   const int64_t steps = hidden / (4 * F::EPC);
   // 16-byte scale pieces need 16-byte aligned scale rows; otherwise one step
   // per slot (the odd slot size loads the scales as 16-bit values)
@@ -584,7 +606,8 @@ bool pick(int64_t hidden, int nb, int mode, int lds_per_block,
     default: return false;
   }
   if (!d->fn) return false;
-  d->lds_bytes = (size_t)(nb + 1) * (size_t)mfma_lds_row_bytes(hidden);
+  d->lds_bytes = (size_t)(nb + 1) * (size_t)mfma_lds_row_bytes(hidden, HB);
+  d->fp8_act = F::FP8_ACT;
   if (mode == OUT_DENSE) {
     // a split unit's parts are added through LDS: one f32x4 per lane and
     // tile of every wave
@@ -596,8 +619,8 @@ bool pick(int64_t hidden, int nb, int mode, int lds_per_block,
 
 }  // namespace
 
-int mfma_max_slice(int64_t hidden, int lds_per_block) {
-  const int64_t row = mfma_lds_row_bytes(hidden);
+int mfma_max_slice(int64_t hidden, int lds_per_block, int h_bytes) {
+  const int64_t row = mfma_lds_row_bytes(hidden, h_bytes);
   // the kernels' static LDS (the finish's tables) comes out of the same
   // budget as the h slice
   int64_t nb = ((int64_t)lds_per_block - MFMA_STATIC_LDS) / row - 1;
@@ -606,7 +629,10 @@ int mfma_max_slice(int64_t hidden, int lds_per_block) {
 }
 
 bool mfma_kernel(int fmt, int64_t hidden, int nb, int mode,
-                 int lds_per_block, KernelDesc* out) {
+                 int lds_per_block, bool fp8_act, KernelDesc* out) {
+  if (fp8_act)  // the W8A8 step: an E4M3 head only
+    return fmt == FMT_E4M3 &&
+           pick<E4m3Fp8>(hidden, nb, mode, lds_per_block, out);
   switch (fmt) {
     case FMT_NVFP4: return pick<Nvfp4>(hidden, nb, mode, lds_per_block, out);
     case FMT_E4M3: return pick<E4m3>(hidden, nb, mode, lds_per_block, out);

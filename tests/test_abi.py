@@ -272,10 +272,11 @@ def test_token_quantize_rejects_bad_arguments_on_the_host():
 
 def test_w8a8_workspace_and_arguments_on_the_host():
     """The W8A8 workspace is the top-token workspace plus the tokens' BF16
-    activations and scales; every call checks it on the host."""
+    activations, their E4M3 codes and scales; every call checks it on the
+    host."""
     base = dh.draft_head_workspace_bytes(98304, 16)
     w = dh.draft_head_workspace_bytes_w8a8(98304, 16, 2560)
-    assert w >= base + 16 * 2560 * 2 + 16 * 4
+    assert w >= base + 16 * 2560 * 2 + 16 * 2560 + 16 * 4
     assert dh.draft_head_workspace_bytes_w8a8(98304, 16, 5120) > w
     assert dh.draft_head_workspace_bytes_w8a8(98304, 16, 40) == 0
     assert dh.draft_head_workspace_bytes_w8a8(0, 16, 2560) == 0
