@@ -212,14 +212,41 @@ __device__ __forceinline__ uint32_t fp8_pair(float a, float b) {
 // The largest bf16 magnitude (bits) of the Markstein quotient's range.
 constexpr uint32_t BF16_2P60 = 0x5D80u;
 
+// The element codes of a lane's 8 elements with divisions and the midpoint
+// count, for a block whose scale code is sc (the slow path below).
+template <bool F16>
+__device__ __forceinline__ uint32_t encode_slow(const uint32_t (&x)[4],
+                                                uint32_t sc, float gs) {
+  const float d = e4m3_decode_nonneg(sc) * gs;
+  uint32_t out = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t bits = (x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+    const float ax = elem_f32<F16>(bits & 0x7FFFu);
+    const uint32_t mag = sc == 0 ? 0u : e2m1_code(ax / d);
+    out |= (((bits >> 15) << 3) | mag) << (4 * e);
+  }
+  return out;
+}
+
 // One lane per 8 elements, two lanes (i, i^1) per 16-element block.  The
 // encode pass walks the tiles from the last to the first: the amax pass has
 // just read the same bytes in the opposite order, so the first tiles read
 // here are the ones most likely still in the device's last-level cache.
-// Per element the fast path is one Markstein quotient and half a hardware
-// convert; a wave that has a block outside the Markstein range (a NaN,
-// |x| > 2^60 or an extreme divisor) encodes the tile with the division and
-// the midpoint count instead.
+//
+// Fast path, per block: s = bmax / (6 gs) as a Markstein quotient (the
+// divisor is the same for the whole call, so its correctly rounded
+// reciprocal is computed once), the E4M3 code of s with the hardware
+// convert (exact: s stays below 449, and the convert rounds to nearest-even
+// up to 464), and the divisor d = e4m3(s) * gs with its correctly rounded
+// reciprocal from a table of the 127 codes that each block builds once.
+// Per element: the Markstein quotient of the signed value (rounding to
+// nearest is symmetric, so it is the signed correctly rounded quotient),
+// the sign of x put back (a zero quotient of a negative x is -0), and half
+// a hardware convert.  A zero scale gives d = 1, rd = 0, so every quotient
+// is a zero of x's sign.  A wave with a block outside these ranges (a NaN or
+// infinity, |x| > 2^60, a divisor outside the Markstein range) encodes its
+// tiles with divisions, the software E4M3 encoder and the midpoint count.
 template <bool F16>
 __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
     const uint16_t* __restrict__ w, int64_t hidden,
@@ -230,6 +257,16 @@ __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
   const int lane = threadIdx.x & 63;
   const float gs = global_scale_from(*amax_bits);
   const float six_gs = 6.0f * gs;
+  const float r_six_gs = 1.0f / six_gs;
+  const bool six_in_range = divisor_in_range(six_gs);
+  // (d, 1/d) of every non-negative E4M3 code; code 0 (a zero scale) as above
+  __shared__ float2 dtab[128];
+  if (threadIdx.x < 128) {
+    const uint32_t c = threadIdx.x;
+    const float d = e4m3_decode_nonneg(c < 0x7Fu ? c : 0x7Eu) * gs;
+    dtab[c] = c == 0 ? make_float2(1.0f, 0.0f) : make_float2(d, 1.0f / d);
+  }
+  __syncthreads();
   const int64_t wave = (int64_t)blockIdx.x * QWAVES +
                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * QWAVES;
@@ -246,42 +283,41 @@ __global__ __launch_bounds__(QTHREADS) void k_nvfp4_encode(
           0, (int)bm, DPP_QUAD_1032, 0xF, 0xF, false);
       bm = bm > other ? bm : other;
       const float bmax = elem_f32<F16>(bm);
-      const float s = bmax / six_gs;
-      const uint32_t sc = e4m3_encode_nonneg(s);
-      const float s_dec = e4m3_decode_nonneg(sc);
-      const float d = s_dec * gs;
-      const bool zero = s_dec == 0.0f;
-      const float rd = 1.0f / d;
-      // (binary16 magnitudes never reach 2^60)
-      const bool fast =
-          zero || (divisor_in_range(d) && (F16 || bm <= BF16_2P60));
       const uint32_t x[4] = {v.x, v.y, v.z, v.w};
-      uint32_t out = 0;
-      if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+      // finite and at most 2^60 (binary16 magnitudes never reach it)
+      const bool x_ok = F16 ? bm < 0x7C00u : bm <= BF16_2P60;
+      uint32_t sc, out = 0;
+      if (__builtin_amdgcn_ballot_w64(!(six_in_range && x_ok)) == 0) {
+        const float q0 = bmax * r_six_gs;
+        const float rr = __builtin_fmaf(-q0, six_gs, bmax);
+        const float s = __builtin_fmaf(rr, r_six_gs, q0);
+        sc = fp8_pair(s, s) & 0xFFu;
+        const float2 dd = dtab[sc & 0x7Fu];  // (s < 449: never the NaN code)
+        const float d = dd.x, rd = dd.y;
+        if (__builtin_amdgcn_ballot_w64(!(sc == 0 || divisor_in_range(d))) ==
+            0) {
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float q[2];
+          for (int e = 0; e < 8; e += 2) {
+            const uint32_t xw = x[e >> 1];
+            float q[2];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t bits = (x[(e + h) >> 1] >> (((e + h) & 1) * 16)) &
-                                  0xFFFFu;
-            const float ax = elem_f32<F16>(bits & 0x7FFFu);
-            const float q0 = ax * rd;
-            const float r = __builtin_fmaf(-q0, d, ax);
-            const float mag = zero ? 0.0f : __builtin_fmaf(r, rd, q0);
-            q[h] = __uint_as_float(__float_as_uint(mag) |
-                                   ((bits & 0x8000u) << 16));
+            for (int h = 0; h < 2; ++h) {
+              const float xs =
+                  F16 ? elem_f32<true>(h ? xw >> 16 : xw & 0xFFFFu)
+                      : __uint_as_float(h ? xw & 0xFFFF0000u : xw << 16);
+              const float a0 = xs * rd;
+              const float ra = __builtin_fmaf(-a0, d, xs);
+              q[h] = __builtin_copysignf(__builtin_fmaf(ra, rd, a0), xs);
+            }
+            out = fp4_pair(out, q[0], q[1], e >> 1);
           }
-          out = fp4_pair(out, q[0], q[1], e >> 1);
+        } else {
+          out = encode_slow<F16>(x, sc, gs);
         }
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bits = (x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          const float ax = elem_f32<F16>(bits & 0x7FFFu);
-          const uint32_t mag = zero ? 0u : e2m1_code(ax / d);
-          out |= (((bits >> 15) << 3) | mag) << (4 * e);
-        }
+        const float s = bmax / six_gs;
+        sc = e4m3_encode_nonneg(s);
+        out = encode_slow<F16>(x, sc, gs);
       }
       if (ld[u].live) {
         const int64_t j = ld[u].j, k = ld[u].k;
