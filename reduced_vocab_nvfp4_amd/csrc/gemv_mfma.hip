@@ -525,14 +525,15 @@ __global__ __launch_bounds__(NT) void k_mfma(const KArgs a) {
 }
 
 // Launch shape: one 16-row tile per unit, a double-buffered ring of slots,
-// one block per CU (the h slice fills most of the LDS), 512 threads (two
-// waves per SIMD, 256 VGPRs each).
+// one block per CU (the h slice fills most of the LDS; see desc), 512
+// threads (two waves per SIMD, 256 VGPRs each).
 //   * NVFP4: slots of four steps.  On the 98K head at batch 16 this is 7%
 //     faster than 1024 threads: the 6144 tiles then make three units for
 //     every wave instead of one and a half, and the extra waves bought no
-//     latency cover.
-//   * E4M3 and BF16: slots of ten steps (ten 1 KB loads per slot), 2%
-//     faster than the NVFP4 shape on the 98K E4M3 head.
+//     latency cover.  768 threads (two units per wave), a third ring slot
+//     and slots of ten steps measured the same or slower.
+//   * E4M3 and BF16 (and the W8A8 codes): slots of ten steps (ten 1 KB
+//     loads per slot), 2% faster than the NVFP4 shape on the 98K E4M3 head.
 constexpr int MFMA_RT = 1;
 constexpr int MFMA_NB = 2;
 
