@@ -38,6 +38,13 @@ def test_library_exports_every_declared_symbol():
     assert dh.error_string(dh.DH_EINVAL).startswith("invalid")
 
 
+def test_build_checks_the_version_the_header_declares():
+    """__graft_entry__.build() compares the library's ABI version with the
+    one include/drafthead.h declares, not with a copy of it."""
+    import __graft_entry__ as ge
+    assert ge.header_abi_version() == dh.lib().drafthead_abi_version()
+
+
 @pytest.mark.parametrize("name", ["tiny", "flash_next_64k", "h98k_b16"])
 def test_build_index_matches_oracle(name):
     keep = wl.keep_mask(wl.WORKLOADS[name])
