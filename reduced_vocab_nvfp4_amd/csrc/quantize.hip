@@ -420,9 +420,19 @@ __global__ __launch_bounds__(QTHREADS) void k_fp8_tokens(
   const int64_t b = blockIdx.x;
   const uint4* row = reinterpret_cast<const uint4*>(h + b * hidden);
   const int n8 = (int)(hidden / 8);
+  // the row stays in registers between the two passes: at most 16 384
+  // values, TOK_U pieces of 8 per thread, all loads issued at once
+  constexpr int TOK_U = 16384 / 8 / QTHREADS;
+  uint4 rv[TOK_U];
+#pragma unroll
+  for (int u = 0; u < TOK_U; ++u) {
+    const int i = threadIdx.x + u * QTHREADS;
+    rv[u] = i < n8 ? row[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
   uint32_t m = 0u;
-  for (int i = threadIdx.x; i < n8; i += QTHREADS) {
-    const uint32_t v = abs_bf16_max8(row[i]);
+#pragma unroll
+  for (int u = 0; u < TOK_U; ++u) {
+    const uint32_t v = abs_bf16_max8(rv[u]);
     m = v > m ? v : m;
   }
 #pragma unroll
@@ -437,8 +447,11 @@ __global__ __launch_bounds__(QTHREADS) void k_fp8_tokens(
   for (int w = 1; w < QWAVES; ++w) m = red[w] > m ? red[w] : m;
   // magnitudes are compared as bf16 bit patterns (monotonic for |x|)
   const float scale = fmaxf(bf16_to_f32(m), 1e-12f) / 448.0f;
-  for (int i = threadIdx.x; i < n8; i += QTHREADS) {
-    const uint4 v = row[i];
+#pragma unroll
+  for (int u = 0; u < TOK_U; ++u) {
+    const int i = threadIdx.x + u * QTHREADS;
+    if (i >= n8) break;
+    const uint4 v = rv[u];
     const uint32_t x[4] = {v.x, v.y, v.z, v.w};
     uint32_t code[2] = {0u, 0u};
 #pragma unroll
@@ -508,6 +521,9 @@ hipError_t launch_nvfp4_quantize(const QuantArgs& a, hipStream_t s) {
 hipError_t launch_fp8_tokens(const uint16_t* h, int64_t batch, int64_t hidden,
                              uint8_t* qx, uint16_t* hq, float* sx,
                              hipStream_t s) {
+  // the kernel holds a row of at most 16 384 values in registers
+  if (batch < 1 || hidden < 8 || hidden > 16384 || hidden % 8 != 0)
+    return hipErrorInvalidValue;
   k_fp8_tokens<<<(unsigned)batch, QTHREADS, 0, s>>>(h, hidden, qx, hq, sx);
   return hipGetLastError();
 }
