@@ -358,6 +358,50 @@ class Case:
         return L, oracle.argmax_remap(L, self.idx)[1]
 
 
+def time_read_probe(case, K, reps, stream):
+    """The plain streaming read of the step's own head buffers, in the same
+    rotation and with the same timing as the step (drafthead_read_probe):
+    the rate at which this device streams those bytes with nothing else to
+    do, the practical ceiling of the step's weight stream.  Median µs per
+    read over the repeats."""
+    L = dh.lib()
+    sp = int(stream.cuda_stream)
+    sink = torch.zeros(1, dtype=torch.int32, device=case.heads[0][0].device)
+    sk = sink.data_ptr()
+    bufs = []
+    for hd in case.heads:
+        a = hd[0]
+        b = hd[1] if len(hd) > 1 else None
+        bufs.append((a.data_ptr(), a.numel() * a.element_size(),
+                     b.data_ptr() if b is not None else None,
+                     b.numel() * b.element_size() if b is not None else 0))
+    R = len(bufs)
+
+    def call(i):
+        pa, na, pb, nb = bufs[i % R]
+        rc = L.drafthead_read_probe(pa, na, pb, nb, sk, sp)
+        if rc != 0:
+            raise RuntimeError(f"drafthead_read_probe: {dh.error_string(rc)}")
+    for i in range(2 * R):
+        call(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    us = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(int(2e7))
+        except (AttributeError, RuntimeError):
+            pass
+        e0.record(stream)
+        for i in range(K):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1000.0 / K)
+    return float(np.median(us))
+
+
 def cpu_baseline(case, h_list, budget_s):
     """The oracle's step (float64 GEMV over every row, then argmax + remap
     or the logits scatter) on the host, repeated on full steps until
@@ -571,6 +615,8 @@ def main():
         rep_us.append(e0.elapsed_time(e1) * 1000.0 / K)
     us_step = float(np.median(rep_us))
     gbs = case.nbytes / (us_step * 1e-6) / 1e9
+    read_us = time_read_probe(case, K, reps, stream)
+    read_gbs = case.head_bytes / (read_us * 1e-6) / 1e9
 
     # ---- parity against the oracle, and the CPU leg -----------------------
     result_cpu, parity = None, None
@@ -661,6 +707,16 @@ def main():
             "rocprof_kernel_us": k_us,
             "rocprof_frac": (round(case.nbytes / (k_us * 1e-6) / 1e9
                                    / HBM_PEAK_GBS, 4) if k_us else None),
+            # a plain streaming read of the same head buffers, timed the same
+            # way in the same run: the step's weight stream against the rate
+            # this device reaches for those bytes with nothing else to do
+            "plain_read": {
+                "us": round(read_us, 3),
+                "bytes": case.head_bytes,
+                "gbs": round(read_gbs, 2),
+                "frac": round(read_gbs / HBM_PEAK_GBS, 4),
+                "step_over_plain_read": round(read_us / us_step, 4),
+            },
         },
         "cpu_baseline": result_cpu,
         "parity": parity,

@@ -79,7 +79,7 @@ extern "C" {
 #define DH_EWORKSPACE (-2) /* workspace pointer null or too small */
 #define DH_EHIP (-3)       /* a HIP runtime call or kernel launch failed */
 
-#define DRAFTHEAD_ABI_VERSION 4
+#define DRAFTHEAD_ABI_VERSION 5
 
 /* Byte offsets of the two uint16 fields of a workspace a caller may read or
  * write (see "Give-up" above). */
@@ -389,6 +389,28 @@ int draft_head_logits_bf16(const void* w_bf16, const int32_t* dh_idx,
                            int64_t vocab, const void* h_bf16, int64_t batch,
                            float* out_logits, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement aid: streams a_bytes at a, then b_bytes at b, once, with
+ * nothing else to do (page 4, "autotrust/Qwen3.8-27B-NVFP4-DGX-SPARK", "Why
+ * native MTP plateaus at 37": a draft step is a stream of lm_head bytes).
+ * Timed on a head's own buffers (codes and scales), it gives the rate at
+ * which the device streams those bytes: the practical ceiling of the
+ * draft-head calls above.  Nothing is computed and nothing written, except
+ * that every wave of the read folds the 32-bit words it read into one XOR
+ * and stores it to sink[0] when it equals DRAFTHEAD_READ_PROBE_MAGIC (so
+ * the reads cannot be skipped, and a buffer that holds the constant once
+ * among zeros shows that every byte was read).
+ *   a      [device] 16-byte aligned, a_bytes a multiple of 16
+ *   b      [device] 16-byte aligned, b_bytes a multiple of 16; NULL when
+ *                   b_bytes is 0
+ *   sink   [device] one uint32, 4-byte aligned
+ * Errors: DH_EINVAL for a null or misaligned pointer, a size that is not a
+ * multiple of 16, or nothing to read; DH_EHIP.
+ */
+#define DRAFTHEAD_READ_PROBE_MAGIC 0x9E3779B9u
+int drafthead_read_probe(const void* a, size_t a_bytes, const void* b,
+                         size_t b_bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.draft_head_top_tokens_noalloc.argtypes = [
             _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64,
             _c_ptr, _c_ptr]
+        L.drafthead_read_probe.restype = ctypes.c_int
+        L.drafthead_read_probe.argtypes = [_c_ptr, _c_size, _c_ptr, _c_size,
+                                           _c_ptr, _c_ptr]
         L.draft_head_logits.restype = ctypes.c_int
         L.draft_head_logits.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_i64, _c_i64, _c_i64, _c_i64,
@@ -295,6 +298,35 @@ def draft_head_top_tokens_noalloc(packed, scales, global_scale, dh_idx, h, *,
         _dev(out_ids, "out_ids", torch.int32), _stream(dev, stream))
     _check("draft_head_top_tokens_noalloc", rc)
     return out_ids
+
+
+# Measurement aid (drafthead_read_probe): the constant a wave's XOR of the
+# words it read must equal for the probe to store it.
+READ_PROBE_MAGIC = 0x9E3779B9
+
+
+def read_probe(a: torch.Tensor, b: torch.Tensor = None, *, sink=None,
+               stream=None) -> torch.Tensor:
+    """One plain streaming read of a's bytes, then b's (contiguous device
+    tensors, 16-byte aligned, sizes multiples of 16 bytes): the device's
+    rate for streaming a head's own buffers.  Returns the sink (int32 [1],
+    written only by a wave whose XOR equals READ_PROBE_MAGIC)."""
+    def ptr(t, name):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return t.data_ptr(), t.numel() * t.element_size()
+    pa, na = ptr(a, "a")
+    pb, nb = ptr(b, "b") if b is not None else (None, 0)
+    if sink is None:
+        with _alloc_stream(stream):
+            sink = torch.zeros(1, dtype=torch.int32, device=a.device)
+    rc = lib().drafthead_read_probe(pa, na, pb, nb,
+                                    _dev(sink, "sink", torch.int32),
+                                    _stream(a.device, stream))
+    _check("drafthead_read_probe", rc)
+    return sink
 
 
 # ------------------------------------------------------------- A5 logits

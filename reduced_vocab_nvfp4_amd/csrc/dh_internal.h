@@ -104,4 +104,8 @@ struct GemvArgs {
 };
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
 
+// The plain streaming read of a then b (drafthead_read_probe).
+hipError_t launch_read_probe(const void* a, size_t a_bytes, const void* b,
+                             size_t b_bytes, uint32_t* sink, hipStream_t s);
+
 }  // namespace dh

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(dh.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared but not exported"
-    assert dh.lib().drafthead_abi_version() == 4
+    assert dh.lib().drafthead_abi_version() == 5
     assert dh.error_string(dh.DH_EINVAL).startswith("invalid")
 
 
@@ -166,6 +166,25 @@ def test_noalloc_top_tokens_rejects_bad_arguments_on_the_host():
     # the largest workspace any batch needs is the scratch's size
     assert (dh.draft_head_workspace_bytes(1 << 20, 64)
             <= 1048832 == dh.draft_head_workspace_bytes(128, 64))
+
+
+def test_read_probe_rejects_bad_arguments_on_the_host():
+    """The measurement aid checks pointers, alignment and sizes before it
+    launches anything."""
+    L = dh.lib()
+
+    def probe(a=FAKE, na=4096, b=FAKE, nb=4096, sink=FAKE):
+        return L.drafthead_read_probe(a, na, b, nb, sink, None)
+    assert probe(a=None) == dh.DH_EINVAL
+    assert probe(sink=None) == dh.DH_EINVAL
+    assert probe(a=FAKE + 8) == dh.DH_EINVAL
+    assert probe(b=FAKE + 4) == dh.DH_EINVAL
+    assert probe(sink=FAKE + 2) == dh.DH_EINVAL
+    assert probe(na=100) == dh.DH_EINVAL
+    assert probe(nb=24) == dh.DH_EINVAL
+    assert probe(na=0, nb=0) == dh.DH_EINVAL
+    assert probe(b=None) == dh.DH_EINVAL          # b_bytes > 0 needs b
+    assert dh.READ_PROBE_MAGIC == 0x9E3779B9
 
 
 def test_e4m3_quantize_rejects_bad_arguments_on_the_host():
