@@ -4,7 +4,10 @@
 // argmax (or the logits scatter) as in the batch-1 kernel.  Page 3
 // ("...MTP-NVFP4-h98k", "How it was built") gives the NVFP4 recipe, page 2
 // the per-tensor E4M3 head; the batch-16 decode step of the 98 304-row head
-// is the workload this kernel is shaped for.
+// is the workload this kernel is shaped for.  Page 2's W8A8 step
+// (_Fp8DraftHeadMethod.apply) runs the same kernel on E4M3 token codes and
+// the head's E4M3 bytes as they are, with v_mfma_f32_16x16x32_fp8_fp8
+// (format E4m3Fp8 in formats.h): no weight decode.
 //
 // MFMA operands (16x16x32, wave64):
 //   A = h          lane l holds 8 BF16 of batch row m = l%16, k-slot group
