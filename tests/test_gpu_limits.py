@@ -2,7 +2,10 @@
 four MFMA slices of 16) and the largest hidden size (16 384, where the MFMA
 kernel stages at most three batch rows per slice and batch 1 runs the
 generic kernel) on the smallest head (64 rows), for every step kind:
-top tokens and logits (fp32 and BF16), the W8A8 head and the linear."""
+top tokens and logits (fp32 and BF16), the W8A8 head and the linear.  At
+hidden 16 384 the W8A8 head's FP8 kernel stages one-byte token codes, eight
+batch rows per slice, so batch 9 runs a slice of eight on the FP8 matrix
+cores and one on the stream kernel."""
 import sys
 
 import numpy as np
@@ -86,3 +89,29 @@ def test_hidden_16384_on_a_64_row_head(B):
     y = dh.nvfp4_linear(pg, sg, gg, hg).cpu().numpy()
     assert H.close(y, L).all()
     say(f"[limits] hidden 16384, 64 rows, B={B}")
+
+
+@pytest.mark.parametrize("B", [3, 9])
+def test_hidden_16384_w8a8(B):
+    rng = np.random.default_rng(620 + B)
+    n, hid, V = 64, 16384, 200000
+    w = torch.from_numpy(rng.standard_normal((n, hid)).astype(np.float32)
+                         * 0.02).to(torch.bfloat16)
+    idx = np.arange(n, dtype=np.int32)
+    q, sc = dh.e4m3_quantize_rows_per_tensor(w.to(DEV),
+                                             torch.from_numpy(idx).to(DEV))
+    oq, osc = oracle.e4m3_tensor_quantize(wl.bf16_bits(w), idx)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    ids_kept = np.sort(rng.permutation(V)[:n]).astype(np.int32)
+    ig = torch.from_numpy(ids_kept).to(DEV)
+    h = wl.hidden_states(B, hid, 630 + B)
+    hg = h.to(DEV)
+    qx, sx = oracle.fp8_tokens_quantize(wl.bf16_bits(h))
+    L = oracle.w8a8_logits(oq, osc, qx, sx)
+    _, want = oracle.argmax_remap(L, ids_kept)
+    ids = dh.draft_head_top_tokens_w8a8(q, sc, ig, hg).cpu().numpy()
+    assert H.check_top_tokens(ids, L, ids_kept, n, want) <= 1
+    out = dh.draft_head_logits_w8a8(q, sc, ig, n, V, hg).cpu().numpy()
+    _logits_ok(out, oracle.logits_scatter(L, n, ids_kept, V),
+               f"W8A8 H=16384 B={B}")
+    say(f"[limits] W8A8 hidden 16384, 64 rows, B={B}")
