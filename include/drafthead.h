@@ -406,7 +406,7 @@ int draft_head_logits_bf16(const void* w_bf16, const int32_t* dh_idx,
  *                   b_bytes is 0
  *   sink   [device] one uint32, 4-byte aligned
  * Errors: DH_EINVAL for a null or misaligned pointer, a size that is not a
- * multiple of 16, or nothing to read; DH_EHIP.
+ * multiple of 16 or above 2^48 bytes, or nothing to read; DH_EHIP.
  */
 #define DRAFTHEAD_READ_PROBE_MAGIC 0x9E3779B9u
 int drafthead_read_probe(const void* a, size_t a_bytes, const void* b,

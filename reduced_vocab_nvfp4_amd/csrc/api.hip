@@ -542,12 +542,16 @@ int draft_head_logits_bf16(const void* w_bf16, const int32_t* dh_idx,
                     workspace, workspace_bytes, stream);
 }
 
+static constexpr size_t kMaxProbeBytes = (size_t)1 << 48;
+
 int drafthead_read_probe(const void* a, size_t a_bytes, const void* b,
                          size_t b_bytes, uint32_t* sink, void* stream) {
   if (!a || !sink || !dh::aligned(a, 16) || !dh::aligned(sink, 4))
     return DH_EINVAL;
   if (a_bytes % 16 != 0 || b_bytes % 16 != 0 || a_bytes + b_bytes == 0)
     return DH_EINVAL;
+  // no buffer is that large; this also keeps the sum from wrapping
+  if (a_bytes > kMaxProbeBytes || b_bytes > kMaxProbeBytes) return DH_EINVAL;
   if (b_bytes != 0 && (!b || !dh::aligned(b, 16))) return DH_EINVAL;
   return dh::status(dh::launch_read_probe(a, a_bytes, b, b_bytes, sink,
                                           static_cast<hipStream_t>(stream)));

@@ -42,6 +42,13 @@ hipError_t launch_fp8_tokens(const uint16_t*, int64_t batch, int64_t hidden,
   ++launches;
   return hipSuccess;
 }
+hipError_t launch_read_probe(const void*, size_t a_bytes, const void*,
+                             size_t b_bytes, uint32_t*, hipStream_t) {
+  if (a_bytes % 16 != 0 || b_bytes % 16 != 0 || a_bytes + b_bytes == 0)
+    return hipErrorInvalidValue;
+  ++launches;
+  return hipSuccess;
+}
 }  // namespace dh
 
 extern "C" hipError_t hipGetDevice(int* d) {
@@ -236,6 +243,9 @@ int main() {
                                   w8, nullptr),
            2);
   LAUNCHED(fp8_quantize_tokens(P, 16, H, P8, PF, nullptr), 1);
+  uint32_t* PU = static_cast<uint32_t*>(P);
+  LAUNCHED(drafthead_read_probe(P, 1 << 20, P, 160 << 10, PU, nullptr), 1);
+  LAUNCHED(drafthead_read_probe(P, 1 << 20, nullptr, 0, PU, nullptr), 1);
 
   // refused shapes and pointers
   REFUSED(draft_head_top_tokens(nullptr, P8, PF, PI, N, H, P, 1, PI, P, ws1,
@@ -301,6 +311,21 @@ int main() {
   REFUSED(fp8_quantize_tokens(P, (1 << 16) + 1, H, P8, PF, nullptr),
           DH_EINVAL);
   REFUSED(fp8_quantize_tokens(P, 4, 40, P8, PF, nullptr), DH_EINVAL);
+  REFUSED(drafthead_read_probe(nullptr, 16, nullptr, 0, PU, nullptr),
+          DH_EINVAL);
+  REFUSED(drafthead_read_probe(MIS, 16, nullptr, 0, PU, nullptr), DH_EINVAL);
+  REFUSED(drafthead_read_probe(P, 24, nullptr, 0, PU, nullptr), DH_EINVAL);
+  REFUSED(drafthead_read_probe(P, 16, nullptr, 16, PU, nullptr), DH_EINVAL);
+  REFUSED(drafthead_read_probe(P, 16, MIS, 16, PU, nullptr), DH_EINVAL);
+  REFUSED(drafthead_read_probe(P, 0, nullptr, 0, PU, nullptr), DH_EINVAL);
+  REFUSED(drafthead_read_probe(P, 16, nullptr, 0, nullptr, nullptr),
+          DH_EINVAL);
+  REFUSED(drafthead_read_probe(P, 16, nullptr, 0,
+                               reinterpret_cast<uint32_t*>(P8 + 2), nullptr),
+          DH_EINVAL);
+  // sizes whose sum wraps around
+  REFUSED(drafthead_read_probe(P, SIZE_MAX - 15, P, 32, PU, nullptr),
+          DH_EINVAL);
 
   printf("C-ABI host sanitizer run: %d launches, %d failures\n", launches,
          failures);
