@@ -84,9 +84,11 @@ def _first_max_rows(vals: np.ndarray) -> np.ndarray:
     return np.argmax(vals, axis=1)  # numpy: the first maximal index
 
 
-def _check_compat_top(ids, L, Lb, idx, n_kept):
+def _check_compat_top(ids, L, Lb, idx, n_kept, row_scale):
     """Returns (exceptions, ties): ties counts batch rows whose BF16 maximum
-    is shared by several kept rows (decided by the lowest-row rule)."""
+    is shared by several kept rows (decided by the lowest-row rule).  The
+    absolute part of the tolerance scales with the batch row's scale (the
+    float32 error of a logit is proportional to the magnitude of h)."""
     vals = oracle.bf16_bits_value(Lb)
     rows = _first_max_rows(vals)
     exc = ties = 0
@@ -99,15 +101,16 @@ def _check_compat_top(ids, L, Lb, idx, n_kept):
         r = np.flatnonzero(idx[:n_kept] == int(ids[b]))
         assert r.size == 1, f"batch {b}: id {ids[b]} is not a kept id"
         lw, lg = L[b, rows[b]], L[b, r[0]]
-        assert abs(lw - lg) <= H.ATOL + H.RTOL * abs(lw), (
+        assert abs(lw - lg) <= H.ATOL * row_scale[b] + H.RTOL * abs(lw), (
             f"batch {b}: got id {ids[b]} (logit {lg}), want {idx[rows[b]]} "
             f"(logit {lw})")
         exc += 1
     return exc, ties
 
 
-def _check_compat_logits(out_bits, L, idx, n_kept, vocab, tag):
-    """out_bits: GPU BF16 [B, V] as uint16."""
+def _check_compat_logits(out_bits, L, idx, n_kept, vocab, tag, row_scale):
+    """out_bits: GPU BF16 [B, V] as uint16; row_scale [B] as in
+    _check_compat_top."""
     Lb = oracle.logits_to_bf16(L)
     ref = oracle.logits_scatter_bf16(Lb, n_kept, idx, vocab)
     bad = out_bits != ref
@@ -116,7 +119,7 @@ def _check_compat_logits(out_bits, L, idx, n_kept, vocab, tag):
         # float32 error of a BF16 rounding boundary: it must then be a BF16
         # value between the roundings of L - err and L + err (near zero that
         # window holds several)
-        err = FP32_ERR_ABS + FP32_ERR_REL * np.abs(L)
+        err = FP32_ERR_ABS * row_scale[:, None] + FP32_ERR_REL * np.abs(L)
         lo = oracle.bf16_bits_value(oracle.logits_scatter_bf16(
             oracle.logits_to_bf16(L - err), n_kept, idx, vocab))
         hi = oracle.bf16_bits_value(oracle.logits_scatter_bf16(
@@ -129,7 +132,8 @@ def _check_compat_logits(out_bits, L, idx, n_kept, vocab, tag):
     assert ((out_bits == 0xFF80).sum(axis=1) == vocab - n_kept).all()
 
 
-def _compat_case(hd, h, tag, packed=None, scales=None, gs=None, o=None):
+def _compat_case(hd, h, tag, packed=None, scales=None, gs=None, o=None,
+                 row_scale=None):
     packed = hd.packed if packed is None else packed
     scales = hd.scales if scales is None else scales
     gs = hd.gs if gs is None else gs
@@ -141,11 +145,12 @@ def _compat_case(hd, h, tag, packed=None, scales=None, gs=None, o=None):
                                       hd.n_kept, hd.vocab, hg)
     bits = out.cpu().view(torch.int16).numpy().view(np.uint16)
     L, Lb = _oracle_compat(o, h)
-    exc, ties = _check_compat_top(ids, L, Lb, hd.idx_o, hd.n_kept)
+    rs = np.ones(h.shape[0]) if row_scale is None else np.asarray(row_scale)
+    exc, ties = _check_compat_top(ids, L, Lb, hd.idx_o, hd.n_kept, rs)
     # the top token is the first maximum of the GPU's own BF16 logits
     kept_vals = oracle.bf16_bits_value(bits[:, hd.idx_o[:hd.n_kept]])
     assert np.array_equal(ids, hd.idx_o[:hd.n_kept][_first_max_rows(kept_vals)])
-    _check_compat_logits(bits, L, hd.idx_o, hd.n_kept, hd.vocab, tag)
+    _check_compat_logits(bits, L, hd.idx_o, hd.n_kept, hd.vocab, tag, rs)
     say(f"[compat top] {tag}: B={h.shape[0]} exceptions={exc} "
         f"bf16 ties at the top={ties}")
     return exc

@@ -11,7 +11,10 @@ BF16 top tokens and logits, and the dense linear.  Rows scaled as a whole
 are compared after dividing by their scale, so the elementwise tolerance
 keeps its meaning (an argmax does not change under a positive scale); the
 other rows unscaled.  Slices of 16 and 5 rows, with hidden 256 (a wave's
-pieces of h span two rows) and 2688 (one-step slots)."""
+pieces of h span two rows) and 2688 (one-step slots).
+
+A row holding an infinity or a NaN leaves the slice's other rows alone, and
+its own logits carry the oracle's pattern of NaN and +-inf."""
 import sys
 
 import numpy as np
@@ -103,9 +106,64 @@ def test_extreme_rows(hidden, B):
     ok = H.close(out[fin] / s[fin], ref[fin] / s[fin])
     assert ok.all(), (tag, np.argwhere(~ok)[:5])
     # BF16 top tokens and logits
-    exc += _compat_case(hd, h, tag)
+    exc += _compat_case(hd, h, tag, row_scale=scale)
     # the dense linear over the kept rows' weights
     y = dh.nvfp4_linear(hd.packed, hd.scales, hd.gs, hg).cpu().numpy()
     ok = H.close(y / scale[:, None], L / scale[:, None])
     assert ok.all(), (tag, np.argwhere(~ok)[:5])
     say(f"[extreme rows] {tag}: near-tie exceptions {exc}")
+
+
+def _zero_weight_column(hd):
+    """The hidden column at which the most kept rows have a zero weight."""
+    lo = hd.o_packed[: hd.n_kept] & 0x7
+    hi = (hd.o_packed[: hd.n_kept] >> 4) & 0x7
+    zeros = np.empty((hd.n_kept, hd.hidden), dtype=bool)
+    zeros[:, 0::2] = lo == 0
+    zeros[:, 1::2] = hi == 0
+    return int(np.argmax(zeros.sum(axis=0)))
+
+
+@pytest.mark.parametrize("hidden", [256, 2560])
+@pytest.mark.parametrize("special", ["inf", "nan"])
+def test_row_with_a_non_finite_element(hidden, special):
+    """Batch row 4 of a 16-row slice holds +inf or NaN at the column where
+    the most head rows have a zero weight.  The other rows' top tokens,
+    fp32 logits and dense linear are the oracle's; row 4's logits have the
+    oracle's pattern of NaN and +-inf (a sum holding a NaN term, or
+    infinities of both signs, is NaN in any order; else it is the infinity:
+    0 * inf makes NaN where the weight is zero)."""
+    hd = _head(hidden)
+    col = _zero_weight_column(hd)
+    B = 16
+    x = np.random.default_rng(970 + hidden).standard_normal((B, hidden))
+    x[4, col] = np.inf if special == "inf" else np.nan
+    h = torch.from_numpy(x).to(torch.bfloat16)
+    tag = f"{special} hidden={hidden} col={col}"
+    say(f"[non-finite row] {tag}")
+    hg = h.to(DEV)
+    L = hd.oracle_logits(h)
+    rows = np.array([b for b in range(B) if b != 4])
+    ids = dh.draft_head_top_tokens(hd.packed, hd.scales, hd.gs, hd.idx_gpu,
+                                   hg).cpu().numpy()
+    _, want = oracle.argmax_remap(L[rows], hd.idx_o)
+    H.check_top_tokens(ids[rows], L[rows], hd.idx_o, hd.n_kept, want)
+    out = dh.draft_head_logits(hd.packed, hd.scales, hd.gs, hd.idx_gpu,
+                               hd.n_kept, hd.vocab, hg).cpu().numpy()
+    ref = oracle.logits_scatter(L, hd.n_kept, hd.idx_o, hd.vocab)
+    fin = np.isfinite(ref[rows])
+    assert np.array_equal(np.isfinite(out[rows]), fin), tag
+    ok = H.close(out[rows][fin], ref[rows][fin])
+    assert ok.all(), (tag, np.argwhere(~ok)[:5])
+    y = dh.nvfp4_linear(hd.packed, hd.scales, hd.gs, hg).cpu().numpy()
+    ok = H.close(y[rows], L[rows])
+    assert ok.all(), (tag, np.argwhere(~ok)[:5])
+    got, want4 = out[4], ref[4]
+    assert np.array_equal(np.isnan(got), np.isnan(want4)), tag
+    assert np.array_equal(np.isposinf(got), np.isposinf(want4)), tag
+    assert np.array_equal(np.isneginf(got), np.isneginf(want4)), tag
+    kept = want4[hd.idx_o[: hd.n_kept]]
+    if special == "inf":  # rows with a zero weight there, and the others
+        assert np.isnan(kept).any() and np.isinf(kept).any(), tag
+    else:
+        assert np.isnan(kept).all(), tag

@@ -179,7 +179,7 @@ def test_bf16_logits_scatter_on_masks_with_long_runs(batch):
             hd.packed, hd.scales, hd.gs, hd.idx_gpu, hd.n_kept, V,
             h.to(DEV)).cpu().view(torch.int16).numpy().view(np.uint16)
         _check_compat_logits(out, hd.logits(h), hd.idx, hd.n_kept, V,
-                             f"{name} B={batch}")
+                             f"{name} B={batch}", np.ones(batch))
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "bf16"])
