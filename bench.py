@@ -530,6 +530,9 @@ def main():
                     help="head copies to rotate (0: enough for 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--seed", type=int, default=0,
+                    help="first hidden-state step: the timed steps use the "
+                         "seeds SEED_H0 + seed .. SEED_H0 + seed + 7")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the timed region, copy a MIB-MiB device "
                          "buffer 5 times (reference for HBM byte counters)")
@@ -568,7 +571,10 @@ def main():
         R = min(4096, -(-2 * INFINITY_CACHE // case.head_bytes) + 1)
     case.rotate(R)
     n_h = 8
-    h_cpu = [wl.hidden_states(B, H, s) for s in range(n_h)]
+    # the timed steps cycle through n_h hidden states, seeds SEED_H0 +
+    # args.seed + i
+    h_steps = [args.seed + i for i in range(n_h)]
+    h_cpu = [wl.hidden_states(B, H, s) for s in h_steps]
     h_gpu = [x.to(dev) for x in h_cpu]
     h_ptrs = [x.data_ptr() for x in h_gpu]
     K, W = args.steps, args.warmup
@@ -692,6 +698,7 @@ def main():
                      "logits": "fp32 logits to the full vocab",
                      "linear": "NVFP4 W4A16 linear, fp32 out"}[case.op],
             "rotated_head_copies": R, "parallelism": "none (1 GPU)",
+            "h_seeds": [wl.SEED_H0 + s for s in h_steps],
         },
         "roofline": {
             "bound": "hbm",
