@@ -537,6 +537,8 @@ def main():
                     help="before the timed region, copy a MIB-MiB device "
                          "buffer 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.seed < 0:
+        ap.error("--seed must be at least 0")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU "

@@ -61,3 +61,11 @@ def test_more_than_one_gpu_is_refused():
                        timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_a_negative_seed_is_refused_before_any_gpu_work():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--seed", "-1"], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 2
+    assert "--seed" in r.stderr
